@@ -1,0 +1,178 @@
+"""Seeded synthetic inputs for the KDA decode op.
+
+This module only draws random numbers and lays them out; it holds none of
+the recurrence's arithmetic.  Both the HIP parity tests and the oracle take
+their inputs from here, and the benchmark draws its workload from here too.
+
+The presets mirror the decode workloads the pages describe: a 96-head layer
+with dk = dv = 128 ("Delta-rule write" page, input/output shapes), the
+Kimi-Linear 32-head shape, a GQA/varlen speculative-window batch and a tiny
+dk = 16 case.  Distributions: q, k, v, raw_gate, beta_logits ~ N(0, 1);
+A_log ~ U(0, ln 16); dt_bias ~ N(0, 0.1); state ~ N(0, sigma).
+
+Draw order from ``numpy.random.default_rng(seed)`` (fixed, so every consumer
+sees identical values): token counts, q, k, v, raw_gate, beta_logits, A_log,
+dt_bias, state indices, and last the touched state tiles (host-state
+workloads only).  bf16 tensors are fp32 draws rounded to nearest-even.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field, replace
+from typing import Optional, Tuple
+
+import numpy as np
+
+SOFTPLUS = "softplus"
+LOWER_BOUND = "lower_bound"
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    HV: int
+    DK: int
+    DV: int
+    n_slots: int
+    tokens: str = "1"                 # "n" fixed per request, or "u:lo..hi"
+    qkv_dtype: str = "bf16"           # "bf16" or "f32"
+    gate_mode: str = SOFTPLUS
+    lower_bound: float = 0.0
+    state_sigma: float = 0.05
+    seed: int = 0
+    cu_seqlens: Optional[Tuple[int, ...]] = None
+    state_indices: Optional[Tuple[int, ...]] = None
+    host_state: bool = False          # draw touched tiles on the host
+    description: str = field(default="", compare=False)
+
+    @property
+    def G(self) -> int:
+        return self.HV // self.H
+
+
+PRESETS = {
+    "tiny": Workload(
+        name="tiny", B=2, H=4, HV=4, DK=16, DV=16, n_slots=4,
+        qkv_dtype="f32", state_sigma=0.1, cu_seqlens=(0, 3, 5),
+        state_indices=(2, 0), host_state=True,
+        description="B=2 (3 and 2 tokens), 4 heads, dk=dv=16, fp32, softplus"),
+    "kimi_b64_h32": Workload(
+        name="kimi_b64_h32", B=64, H=32, HV=32, DK=128, DV=128, n_slots=256,
+        description="B=64, 1 token, 32 heads, dk=dv=128, bf16, softplus"),
+    "varlen_gqa_b128": Workload(
+        name="varlen_gqa_b128", B=128, H=16, HV=32, DK=128, DV=128,
+        n_slots=512, tokens="u:1..8", gate_mode=LOWER_BOUND, lower_bound=-5.0,
+        description="B=128, 1..8 tokens, 16 key / 32 value heads, lower-bound gate"),
+    "wide_b256_h96": Workload(
+        name="wide_b256_h96", B=256, H=96, HV=96, DK=128, DV=128, n_slots=512,
+        description="B=256, 1 token, 96 heads, dk=dv=128, bf16, softplus"),
+    "stress_b1024_n4": Workload(
+        name="stress_b1024_n4", B=1024, H=96, HV=96, DK=128, DV=128,
+        n_slots=2048, tokens="4", gate_mode=LOWER_BOUND, lower_bound=-5.0,
+        description="B=1024, 4 tokens, 96 heads, lower-bound gate"),
+}
+
+HEADLINE = "wide_b256_h96"
+
+
+def preset(name: str, **overrides) -> Workload:
+    return replace(PRESETS[name], **overrides)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bfloat16 (nearest, ties to even); return the bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    nan = np.isnan(np.asarray(x, dtype=np.float32))
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    bits = rounded.astype(np.uint16)
+    bits[nan] = 0x7FC0
+    return bits
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+@dataclass
+class Inputs:
+    """One drawn batch.  Float tensors are fp32 arrays holding the exact values
+    the device sees; for bf16 tensors ``bits`` holds the stored bit patterns."""
+    cfg: Workload
+    cu_seqlens: np.ndarray            # int32 [B+1]
+    state_indices: np.ndarray         # int32 [B]
+    q: np.ndarray                     # [1, T, H, DK]
+    k: np.ndarray
+    v: np.ndarray                     # [1, T, HV, DV]
+    raw_gate: np.ndarray              # fp32 [1, T, HV, DK]
+    beta_logits: np.ndarray           # fp32 [1, T, HV]
+    a_log: np.ndarray                 # fp32 [HV]
+    dt_bias: np.ndarray               # fp32 [HV, DK]
+    bits: dict                        # name -> uint16 bf16 bits
+    touched_state: Optional[np.ndarray] = None   # fp32 [B, HV, DK, DV] (host_state)
+
+    @property
+    def T(self) -> int:
+        return int(self.cu_seqlens[-1])
+
+
+def _token_counts(cfg: Workload, rng: np.random.Generator) -> np.ndarray:
+    if cfg.cu_seqlens is not None:
+        return np.diff(np.asarray(cfg.cu_seqlens, dtype=np.int64))
+    if cfg.tokens.startswith("u:"):
+        lo, hi = (int(s) for s in cfg.tokens[2:].split(".."))
+        return rng.integers(lo, hi + 1, size=cfg.B)
+    return np.full(cfg.B, int(cfg.tokens), dtype=np.int64)
+
+
+def draw(cfg: Workload) -> Inputs:
+    rng = np.random.default_rng(cfg.seed)
+    counts = _token_counts(cfg, rng)
+    cu = np.zeros(cfg.B + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(counts)
+    T = int(cu[-1])
+
+    def normal(shape, sigma=1.0):
+        return (rng.standard_normal(size=shape, dtype=np.float32) * np.float32(sigma)).astype(np.float32)
+
+    q = normal((1, T, cfg.H, cfg.DK))
+    k = normal((1, T, cfg.H, cfg.DK))
+    v = normal((1, T, cfg.HV, cfg.DV))
+    raw_gate = normal((1, T, cfg.HV, cfg.DK))
+    beta_logits = normal((1, T, cfg.HV))
+    a_log = rng.uniform(0.0, math.log(16.0), size=cfg.HV).astype(np.float32)
+    dt_bias = normal((cfg.HV, cfg.DK), 0.1)
+    if cfg.state_indices is not None:
+        idx = np.asarray(cfg.state_indices, dtype=np.int32)
+    else:
+        idx = rng.permutation(cfg.n_slots)[: cfg.B].astype(np.int32)
+
+    bits = {}
+    if cfg.qkv_dtype == "bf16":
+        for name, arr in (("q", q), ("k", k), ("v", v)):
+            bits[name] = f32_to_bf16_bits(arr)
+        q, k, v = (bf16_bits_to_f32(bits[n]) for n in ("q", "k", "v"))
+    elif cfg.qkv_dtype != "f32":
+        raise ValueError(cfg.qkv_dtype)
+
+    touched = None
+    if cfg.host_state:
+        touched = normal((cfg.B, cfg.HV, cfg.DK, cfg.DV), cfg.state_sigma)
+    return Inputs(cfg, cu, idx, q, k, v, raw_gate, beta_logits, a_log, dt_bias,
+                  bits, touched)
+
+
+def host_pool(inp: Inputs, fill_sigma: Optional[float] = None, seed_offset: int = 1) -> np.ndarray:
+    """Full fp32 pool on the host: the touched tiles from ``inp`` and every
+    other slot drawn from its own generator (seed + seed_offset)."""
+    cfg = inp.cfg
+    rng = np.random.default_rng(cfg.seed + seed_offset)
+    sigma = cfg.state_sigma if fill_sigma is None else fill_sigma
+    pool = (rng.standard_normal((cfg.n_slots, cfg.HV, cfg.DK, cfg.DV), dtype=np.float32)
+            * np.float32(sigma)).astype(np.float32)
+    if inp.touched_state is not None:
+        for b, slot in enumerate(inp.state_indices):
+            if slot >= 0:
+                pool[slot] = inp.touched_state[b]
+    return pool
