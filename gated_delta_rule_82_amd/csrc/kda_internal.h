@@ -1,0 +1,36 @@
+// kda_internal.h - what the argument checker hands to the kernel launcher.
+#ifndef KDA_INTERNAL_H_
+#define KDA_INTERNAL_H_
+
+#include <cstdint>
+
+#include "kda.h"
+
+namespace kda {
+
+// Validated, flattened arguments of one decode call (device pointers).
+struct DecodeArgs {
+  void* out;                    // [T, HV, dv]   bf16 or f32
+  const void* q;                // [T, H, dk]    bf16 or f32
+  const void* k;                // [T, H, dk]
+  const void* v;                // [T, HV, dv]
+  const float* raw_gate;        // [T, HV, dk]
+  const float* beta_logits;     // [T, HV]
+  const float* a_log;           // [HV]
+  const float* dt_bias;         // [HV, dk]
+  const int32_t* cu_seqlens;    // [B + 1]
+  float* state_pool;            // [N, HV, dk, dv]
+  const int32_t* state_indices; // [B]
+  int32_t B, T, H, HV, G, N;
+  float lower_bound, l2_eps, scale;
+};
+
+// Enqueue the decode kernel for (dk, dv, qkv dtype, gate mode) on `stream`.
+// Returns KDA_OK, KDA_ERR_UNSUPPORTED (no such specialization) or
+// KDA_ERR_LAUNCH.  Defined in kda_decode.hip.
+int launch_decode(const DecodeArgs& args, int dk, int dv, bool bf16, int gate_mode,
+                  hipStream_t stream);
+
+}  // namespace kda
+
+#endif  // KDA_INTERNAL_H_

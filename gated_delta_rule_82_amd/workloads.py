@@ -176,3 +176,70 @@ def host_pool(inp: Inputs, fill_sigma: Optional[float] = None, seed_offset: int 
             if slot >= 0:
                 pool[slot] = inp.touched_state[b]
     return pool
+
+
+# ----------------------------------------------------------------------------
+# device copies (torch is used only for device memory)
+# ----------------------------------------------------------------------------
+
+def to_device(inp: Inputs, device="cuda"):
+    """Upload the token tensors and metadata; returns a dict of torch tensors
+    keyed like the kda_decode arguments (no state pool, no output)."""
+    import torch
+
+    def f32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+
+    def qkv(name, arr):
+        if inp.cfg.qkv_dtype == "bf16":
+            bits = np.ascontiguousarray(inp.bits[name]).view(np.int16)
+            return torch.from_numpy(bits).view(torch.bfloat16).to(device)
+        return f32(arr)
+
+    return {
+        "q": qkv("q", inp.q), "k": qkv("k", inp.k), "v": qkv("v", inp.v),
+        "raw_gate": f32(inp.raw_gate), "beta_logits": f32(inp.beta_logits),
+        "a_log": f32(inp.a_log), "dt_bias": f32(inp.dt_bias),
+        "cu_seqlens": torch.from_numpy(inp.cu_seqlens.astype(np.int32)).to(device),
+        "state_indices": torch.from_numpy(inp.state_indices.astype(np.int32)).to(device),
+    }
+
+
+def empty_out(inp: Inputs, device="cuda"):
+    import torch
+    dt = torch.bfloat16 if inp.cfg.qkv_dtype == "bf16" else torch.float32
+    return torch.empty((1, inp.T, inp.cfg.HV, inp.cfg.DV), dtype=dt, device=device)
+
+
+def device_pool(inp: Inputs, device="cuda", seed_offset: int = 1):
+    """The fp32 state pool on the device.  Host-state workloads upload
+    ``host_pool``; the others are filled on the device from torch's seeded
+    generator (N(0, sigma)), which keeps multi-GB pools off the host."""
+    import torch
+    cfg = inp.cfg
+    if cfg.host_state:
+        return torch.from_numpy(host_pool(inp, seed_offset=seed_offset)).to(device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(cfg.seed + seed_offset)
+    pool = torch.empty((cfg.n_slots, cfg.HV, cfg.DK, cfg.DV), dtype=torch.float32, device=device)
+    pool.normal_(0.0, cfg.state_sigma, generator=gen)
+    return pool
+
+
+def state_bytes(cfg: Workload, inp: Inputs) -> int:
+    """Algorithmic state traffic of one call: every (request, value head) tile
+    with at least one token and a valid slot is read once and written once."""
+    counts = np.diff(inp.cu_seqlens)
+    active = int(np.sum((counts > 0) & (inp.state_indices >= 0)))
+    return active * cfg.HV * 2 * cfg.DK * cfg.DV * 4
+
+
+def token_bytes(cfg: Workload, inp: Inputs) -> int:
+    """Algorithmic bytes of everything but the state, counted once each:
+    q, k (per key head), v, raw_gate, beta_logits, out, a_log, dt_bias and
+    the two metadata arrays."""
+    T = inp.T
+    e = 2 if cfg.qkv_dtype == "bf16" else 4
+    return (2 * T * cfg.H * cfg.DK * e + T * cfg.HV * cfg.DV * e + T * cfg.HV * cfg.DK * 4
+            + T * cfg.HV * 4 + T * cfg.HV * cfg.DV * e + cfg.HV * 4 + cfg.HV * cfg.DK * 4
+            + (cfg.B + 1) * 4 + cfg.B * 4)

@@ -1,0 +1,157 @@
+/*
+ * kda.h - C ABI of libkda, the MI355X (gfx950) KDA decode library.
+ *
+ * One call advances the Kimi Delta Attention recurrence of every
+ * (request, value head) of a decode batch by that request's tokens.  The
+ * operation and the tensor contract follow:
+ *   - "KdaDecode" (Modular MAX Mojo builtin kernels), Tensor Shapes and
+ *     default parameters: packed [1, total_T, ...] token tensors, a slotted
+ *     key-first state pool [max_slots, HV, dk, dv] mutated in place through
+ *     state_indices, cu_seqlens varlen packing, the "original" stable-softplus
+ *     gate and beta given as logits;
+ *   - "Delta-rule write" (atlas, Kimi-K3 > Kimi Delta Attention), code
+ *     excerpt naive_recurrent_kda: per token, decay the state row k by
+ *     exp(g[k]), write (beta*k) outer (v - k^T S), read o = q^T S from the
+ *     updated state; q and k repeated over G = HV/H value heads; the output
+ *     takes v's dtype;
+ *   - "KDA Block TKG Kernel API Reference" (AWS Neuron NKI): l2_eps = 1e-6,
+ *     the query scale folded into the L2-normalised query, and the
+ *     lower-bound gate (parameters A_log, dt_bias, lower_bound).
+ *
+ * Per token t of request b, for value head hv with key head h = hv / G and
+ * state S = state_pool[state_indices[b], hv] (fp32, S[k][v]):
+ *     qh = scale * q[t,h] / sqrt(sum q[t,h]^2 + l2_eps)
+ *     kh =         k[t,h] / sqrt(sum k[t,h]^2 + l2_eps)
+ *     x  = raw_gate[t,hv] + dt_bias[hv]                       (per channel)
+ *     g  = -exp(a_log[hv]) * softplus(x)           (KDA_GATE_SOFTPLUS)
+ *     g  = lower_bound * sigmoid(exp(a_log[hv]) * x)  (KDA_GATE_LOWER_BOUND)
+ *     beta = sigmoid(beta_logits[t,hv])
+ *     S[k][:] *= exp(g[k]);  u = v[t,hv] - kh^T S;  S += beta * kh u^T
+ *     out[t,hv] = qh^T S                         (rounded to nearest-even)
+ * and S is written back to the same slot after the request's last token.
+ *
+ * Memory: every pointer is device memory of the current HIP device, owned
+ * by the caller.  The library allocates nothing, keeps no pointer after the
+ * call returns and holds no state; it is reentrant.  The work is enqueued on
+ * `stream` and the call returns without waiting for it.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* hipStream_t, declared here so that this header needs no HIP include. */
+typedef struct ihipStream_t* hipStream_t;
+
+#define KDA_ABI_VERSION 1
+
+/* Status codes.  Zero is success; errors are negative. */
+enum kda_status {
+  KDA_OK = 0,
+  KDA_ERR_NULL = -1,        /* a required pointer (struct or data) is NULL  */
+  KDA_ERR_DTYPE = -2,       /* a tensor has a dtype this argument rejects   */
+  KDA_ERR_SHAPE = -3,       /* ranks or extents disagree (incl. HV % H)     */
+  KDA_ERR_UNSUPPORTED = -4, /* dk or dv outside {16, 32, 64, 128}, or a    */
+                            /* mix of dtypes that has no kernel             */
+  KDA_ERR_MODE = -5,        /* bad gate mode, lower_bound, l2_eps or scale  */
+  KDA_ERR_LAUNCH = -6,      /* the HIP launch itself reported an error      */
+  KDA_ERR_PRECONDITION = -7 /* kda_check_host: cu_seqlens / indices invalid */
+};
+
+/* Element types of kda_tensor. */
+enum kda_dtype {
+  KDA_F32 = 0,
+  KDA_BF16 = 1,
+  KDA_I32 = 2
+};
+
+/* Gate activation, "KdaDecode" gate_mode / "KDA Block TKG" lower_bound. */
+enum kda_gate_mode {
+  KDA_GATE_SOFTPLUS = 0,    /* g = -exp(A_log) * softplus(x)              */
+  KDA_GATE_LOWER_BOUND = 1  /* g = lower_bound * sigmoid(exp(A_log) * x)  */
+};
+
+/* A dense row-major tensor: `data` points at element [0,...,0]; the extents
+ * are shape[0..ndim-1] and the storage is contiguous (no strides). */
+typedef struct kda_tensor {
+  void* data;
+  int32_t dtype;     /* enum kda_dtype */
+  int32_t ndim;      /* 1..4           */
+  int64_t shape[4];
+} kda_tensor;
+
+/* Scalar parameters of a call. */
+typedef struct kda_mode {
+  int32_t gate_mode;   /* enum kda_gate_mode                                  */
+  float lower_bound;   /* lower-bound mode only: finite and <= 0              */
+  float l2_eps;        /* >= 0, finite; 0 selects the default 1e-6            */
+  float scale;         /* > 0, finite; 0 selects the default dk^-0.5          */
+} kda_mode;
+
+/*
+ * kda_decode - advance the decode recurrence; see the operation above.
+ *
+ * Arguments (B requests, T packed tokens, H key heads, HV value heads,
+ * N pool slots, dk = key/query head size, dv = value head size):
+ *   out           [1, T, HV, dv]  bf16 or f32, must equal v's dtype.  Written
+ *                                 for every token of every request.
+ *   q, k          [1, T, H, dk]   bf16 or f32 (same dtype as v).
+ *   v             [1, T, HV, dv]  bf16 or f32.
+ *   raw_gate      [1, T, HV, dk]  f32, gate pre-activation before dt_bias.
+ *   beta_logits   [1, T, HV]      f32.
+ *   a_log         [HV]            f32.
+ *   dt_bias       [HV, dk]        f32.
+ *   cu_seqlens    [B + 1]         i32, device resident.
+ *   state_pool    [N, HV, dk, dv] f32, key-first, updated in place.
+ *   state_indices [B]             i32, device resident.
+ *   mode          scalar parameters (see kda_mode).
+ *   stream        HIP stream to enqueue on (NULL = the null stream).
+ *
+ * Preconditions on the device-resident metadata, not checked by this call
+ * (checking them would need a device-to-host copy; kda_check_host does it):
+ *   cu_seqlens[0] == 0, non-decreasing, cu_seqlens[B] == T; state_indices
+ *   pairwise distinct among entries >= 0, and < N.
+ * Conventions: state_indices[b] < 0 skips request b: its state is not read
+ *   or written and its output rows are set to zero.  A request with no
+ *   tokens leaves its state untouched.  The kernel clamps every token range
+ *   to [0, T) and treats an index >= N like a negative one, so a violated
+ *   precondition never makes it access memory outside the tensors; duplicate
+ *   indices, however, race and give undefined state.
+ * Errors: every argument check runs before any device work; on a nonzero
+ *   return nothing has been enqueued or written.  KDA_ERR_LAUNCH reports a
+ *   launch error from the HIP runtime.
+ */
+int kda_decode(const kda_tensor* out, const kda_tensor* q, const kda_tensor* k,
+               const kda_tensor* v, const kda_tensor* raw_gate,
+               const kda_tensor* beta_logits, const kda_tensor* a_log,
+               const kda_tensor* dt_bias, const kda_tensor* cu_seqlens,
+               const kda_tensor* state_pool, const kda_tensor* state_indices,
+               const kda_mode* mode, hipStream_t stream);
+
+/*
+ * kda_check_host - validate host copies of the decode metadata.
+ *   cu_seqlens: B + 1 int32 entries; state_indices: B int32 entries.
+ * Returns KDA_OK when cu_seqlens[0] == 0, it is non-decreasing and ends at T,
+ * and the non-negative indices are distinct and < n_slots; KDA_ERR_NULL for
+ * NULL arrays (B > 0), KDA_ERR_SHAPE for B < 0, T < 0 or n_slots < 0, and
+ * KDA_ERR_PRECONDITION otherwise.  Pure host code: no HIP call.
+ */
+int kda_check_host(const int32_t* cu_seqlens, const int32_t* state_indices,
+                   int64_t B, int64_t T, int64_t n_slots);
+
+/* Static description of a status code; never NULL. */
+const char* kda_status_string(int status);
+
+/* KDA_ABI_VERSION of the built library. */
+int kda_abi_version(void);
+
+#ifdef __cplusplus
+}  /* extern "C" */
+#endif
+
+#endif  /* KDA_H_ */

@@ -1,0 +1,170 @@
+"""Shared GPU-test plumbing: run the HIP path through the C ABI binding and
+compare it with the fp64 oracle on the same seeded inputs.
+
+Tolerances (fixed here, used by every GPU parity test):
+  * fp32 state, per (request, head) tile: max|dS| / max|S_ref| <= 1e-4
+    (required bound) and <= STATE_TIGHT (what fp32 arithmetic gives).
+  * bf16 output: max|do| <= 2e-2 absolute (required bound) and, per element,
+    |o_gpu - o_ref| <= 1 bf16 ulp of o_ref + 1e-5 * max|o_ref| (the rounding
+    to bf16 costs half an ulp; fp32 arithmetic adds far less than the rest).
+  * fp32 output: max|do| / max|o_ref| <= 1e-5.
+  * state_indices gathers: every slot not named in state_indices is
+    bit-identical after the call.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from gated_delta_rule_82_amd import workloads as wl
+from oracle import kda_oracle as ko
+
+STATE_REQUIRED = 1e-4
+STATE_TIGHT = 2e-6
+OUT_ABS_REQUIRED = 2e-2
+OUT_ULP_FLOOR = 1e-5
+OUT_F32_REL = 1e-5
+
+
+def bf16_ulp(x):
+    """Spacing of bfloat16 values at |x| (subnormal spacing below 2^-126)."""
+    _, e = np.frexp(np.abs(np.asarray(x, dtype=np.float64)))
+    return np.ldexp(1.0, np.maximum(e - 8, -133))
+
+
+def out_to_f64(out_t):
+    import torch
+    return out_t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
+
+
+def gather_tiles(pool_t, slots, hvs):
+    import torch
+    s = torch.as_tensor(np.asarray(slots, dtype=np.int64), device=pool_t.device)
+    h = torch.as_tensor(np.asarray(hvs, dtype=np.int64), device=pool_t.device)
+    return pool_t[s, h].cpu().numpy()
+
+
+def choose_tiles(inp, sample, seed=123):
+    cfg = inp.cfg
+    all_tiles = [(b, hv) for b in range(cfg.B) for hv in range(cfg.HV)]
+    if sample is None or sample >= len(all_tiles):
+        return all_tiles
+    rng = np.random.default_rng(seed)
+    pick = rng.choice(len(all_tiles), size=sample, replace=False)
+    # always include the first and the last tile (grid edges)
+    chosen = {all_tiles[0], all_tiles[-1]} | {all_tiles[i] for i in pick}
+    return sorted(chosen)
+
+
+def run_gpu(inp, dev, pool_t, out_t=None, mode_overrides=None, stream=None):
+    from gated_delta_rule_82_amd import kda
+    cfg = inp.cfg
+    if out_t is None:
+        out_t = wl.empty_out(inp, pool_t.device)
+    mode = dict(gate_mode=cfg.gate_mode, lower_bound=cfg.lower_bound)
+    if mode_overrides:
+        mode.update(mode_overrides)
+    kda.decode(out_t, dev["q"], dev["k"], dev["v"], dev["raw_gate"], dev["beta_logits"],
+               dev["a_log"], dev["dt_bias"], dev["cu_seqlens"], pool_t, dev["state_indices"],
+               stream=stream, **mode)
+    return out_t
+
+
+def oracle_tiles(inp, tiles, init_states, **mode):
+    """Oracle over ``tiles``; ``init_states`` holds the initial state of each
+    tile whose request has a valid slot, in the order of ``tiles``."""
+    cfg = inp.cfg
+    pool = {}
+    valid = [(b, hv) for b, hv in tiles if inp.state_indices[b] >= 0]
+    assert len(valid) == len(init_states)
+    for (b, hv), S in zip(valid, init_states):
+        pool[(int(inp.state_indices[b]), hv)] = S
+    kw = dict(gate_mode=cfg.gate_mode,
+              lower_bound=cfg.lower_bound if cfg.gate_mode == ko.GATE_LOWER_BOUND else None)
+    kw.update(mode)
+    return ko.kda_decode(inp.q, inp.k, inp.v, inp.raw_gate, inp.beta_logits, inp.a_log,
+                         inp.dt_bias, inp.cu_seqlens, pool, inp.state_indices, tiles=tiles, **kw)
+
+
+def compare_outputs(inp, tiles, out_gpu, out_ref):
+    """Element checks on the output rows of the chosen tiles; returns stats."""
+    cfg = inp.cfg
+    rows_g, rows_r = [], []
+    for b, hv in tiles:
+        t0, t1 = int(inp.cu_seqlens[b]), int(inp.cu_seqlens[b + 1])
+        if t1 > t0:
+            rows_g.append(out_gpu[0, t0:t1, hv])
+            rows_r.append(out_ref[0, t0:t1, hv])
+    if not rows_g:
+        return {"out_max_abs": 0.0}
+    g = np.concatenate(rows_g)
+    r = np.concatenate(rows_r)
+    assert np.isfinite(g).all(), "non-finite output"
+    diff = np.abs(g - r)
+    scale = float(np.max(np.abs(r))) if r.size else 0.0
+    stats = {"out_max_abs": float(diff.max()), "out_ref_max": scale}
+    if cfg.qkv_dtype == "bf16":
+        assert diff.max() <= OUT_ABS_REQUIRED, f"bf16 out abs err {diff.max():.3e} > {OUT_ABS_REQUIRED}"
+        bound = bf16_ulp(r) + OUT_ULP_FLOOR * scale
+        worst = float(np.max(diff / bound))
+        stats["out_ulp_ratio"] = worst
+        assert worst <= 1.0, f"bf16 out exceeds 1 ulp + floor (ratio {worst:.3f})"
+    else:
+        rel = float(diff.max() / max(scale, 1e-30))
+        stats["out_rel"] = rel
+        assert rel <= OUT_F32_REL, f"fp32 out rel err {rel:.3e} > {OUT_F32_REL}"
+    return stats
+
+
+def compare_states(states_gpu, states_ref):
+    worst = 0.0
+    for Sg, Sr in zip(states_gpu, states_ref):
+        denom = float(np.max(np.abs(Sr)))
+        err = float(np.max(np.abs(Sg.astype(np.float64) - Sr)))
+        rel = err / denom if denom > 0 else err
+        worst = max(worst, rel)
+    assert worst <= STATE_REQUIRED, f"state rel err {worst:.3e} > {STATE_REQUIRED}"
+    assert worst <= STATE_TIGHT, f"state rel err {worst:.3e} > tight bound {STATE_TIGHT}"
+    return {"state_rel": worst}
+
+
+def parity_case(inp, device="cuda", sample=None, check_untouched=True, mode_overrides=None,
+                oracle_mode=None, pool_t=None):
+    """Run one batch on the GPU and check it against the oracle.  Returns a
+    dict with the observed errors."""
+    import torch
+    cfg = inp.cfg
+    dev = wl.to_device(inp, device)
+    if pool_t is None:
+        pool_t = wl.device_pool(inp, device)
+    tiles = choose_tiles(inp, sample)
+    valid = [(b, hv) for b, hv in tiles if inp.state_indices[b] >= 0]
+    slots = [int(inp.state_indices[b]) for b, hv in valid]
+    hvs = [hv for b, hv in valid]
+    init = gather_tiles(pool_t, slots, hvs) if valid else []
+    before = pool_t.clone() if check_untouched else None
+    out_t = wl.empty_out(inp, device)
+    out_t.fill_(float("nan"))
+    run_gpu(inp, dev, pool_t, out_t, mode_overrides)
+    torch.cuda.synchronize()
+    out_gpu = out_to_f64(out_t)
+    after = gather_tiles(pool_t, slots, hvs) if valid else []
+
+    out_ref, pool_ref = oracle_tiles(inp, tiles, init, **(oracle_mode or {}))
+    stats = compare_outputs(inp, tiles, out_gpu, out_ref)
+    ref_states = [pool_ref[(s, hv)] for s, hv in zip(slots, hvs)]
+    stats.update(compare_states(after, ref_states) if valid else {})
+    # skipped requests: zero rows
+    for b, hv in tiles:
+        if inp.state_indices[b] < 0:
+            t0, t1 = int(inp.cu_seqlens[b]), int(inp.cu_seqlens[b + 1])
+            assert np.all(out_gpu[0, t0:t1, hv] == 0.0)
+    if check_untouched:
+        touched = sorted({int(s) for s, c in zip(inp.state_indices, np.diff(inp.cu_seqlens))
+                          if s >= 0 and c > 0})
+        mask = torch.ones(cfg.n_slots, dtype=torch.bool, device=pool_t.device)
+        if touched:
+            mask[torch.as_tensor(touched, device=pool_t.device)] = False
+        assert torch.equal(pool_t[mask], before[mask]), "a slot outside state_indices changed"
+        del before
+    stats["tiles"] = len(tiles)
+    return stats, out_t, pool_t

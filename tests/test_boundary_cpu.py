@@ -1,0 +1,196 @@
+"""CPU tests of the C ABI: the library loads, exports what include/kda.h
+declares, and rejects every malformed call before any device work.
+
+No test here launches a kernel: each kda_decode call below is either
+invalid (the checker returns before any HIP call) or has nothing to do
+(B = 0 or T = 0, which return before the launch).  The data pointers are
+fake aligned addresses that are never dereferenced.
+"""
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from gated_delta_rule_82_amd import kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(kda.LIB_PATH),
+                                reason="libkda.so not built (run the build first)")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(kda_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_expected_api():
+    assert header_functions() == sorted(kda.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = kda.library()
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    nm = subprocess.run(["nm", "-D", "--defined-only", kda.LIB_PATH], capture_output=True,
+                        text=True, check=True).stdout
+    exported = {line.split()[-1] for line in nm.splitlines() if " T " in line}
+    assert exported == set(header_functions())
+
+
+def test_abi_version_and_status_strings():
+    lib = kda.library()
+    assert lib.kda_abi_version() == 1
+    codes = [kda.KDA_OK, kda.KDA_ERR_NULL, kda.KDA_ERR_DTYPE, kda.KDA_ERR_SHAPE,
+             kda.KDA_ERR_UNSUPPORTED, kda.KDA_ERR_MODE, kda.KDA_ERR_LAUNCH,
+             kda.KDA_ERR_PRECONDITION]
+    strings = [kda.status_string(c) for c in codes]
+    assert len(set(strings)) == len(codes)
+    assert kda.status_string(12345) == "unknown status"
+
+
+# ---------------------------------------------------------------------------
+# kda_check_host
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cu,idx,T,N,expect", [
+    ([0, 3, 5], [2, 0], 5, 4, kda.KDA_OK),
+    ([0, 3, 5], [2, -1], 5, 4, kda.KDA_OK),
+    ([0, 0, 0], [1, 2], 0, 4, kda.KDA_OK),
+    ([0], [], 0, 0, kda.KDA_OK),
+    ([1, 3, 5], [2, 0], 5, 4, kda.KDA_ERR_PRECONDITION),     # cu[0] != 0
+    ([0, 3, 4], [2, 0], 5, 4, kda.KDA_ERR_PRECONDITION),     # cu[B] != T
+    ([0, 3, 2, 5], [1, 2, 3], 5, 4, kda.KDA_ERR_PRECONDITION),  # decreasing
+    ([0, 3, 5], [2, 2], 5, 4, kda.KDA_ERR_PRECONDITION),     # duplicate slot
+    ([0, 3, 5], [2, 4], 5, 4, kda.KDA_ERR_PRECONDITION),     # slot >= N
+    ([0, 3, 5], [-1, -1], 5, 4, kda.KDA_OK),                 # negatives may repeat
+])
+def test_check_host(cu, idx, T, N, expect):
+    assert kda.check_host(cu, idx, T, N) == expect
+
+
+def test_check_host_bad_sizes_and_nulls():
+    lib = kda.library()
+    assert lib.kda_check_host(None, None, 0, 0, 0) == kda.KDA_ERR_NULL
+    cu = np.array([0, 1], dtype=np.int32)
+    P = __import__("ctypes").POINTER(__import__("ctypes").c_int32)
+    assert lib.kda_check_host(cu.ctypes.data_as(P), None, 1, 1, 4) == kda.KDA_ERR_NULL
+    assert lib.kda_check_host(cu.ctypes.data_as(P), None, -1, 1, 4) == kda.KDA_ERR_SHAPE
+    assert lib.kda_check_host(cu.ctypes.data_as(P), None, 1, -1, 4) == kda.KDA_ERR_SHAPE
+
+
+# ---------------------------------------------------------------------------
+# kda_decode argument checking (never reaches a launch)
+# ---------------------------------------------------------------------------
+
+_FAKE = [0x100000 * (i + 1) for i in range(11)]
+
+
+def descriptors(B=2, T=3, H=2, HV=4, DK=128, DV=128, N=8, qkv=kda.KDA_BF16):
+    shapes = {
+        "out": (qkv, (1, T, HV, DV)), "q": (qkv, (1, T, H, DK)), "k": (qkv, (1, T, H, DK)),
+        "v": (qkv, (1, T, HV, DV)), "raw_gate": (kda.KDA_F32, (1, T, HV, DK)),
+        "beta_logits": (kda.KDA_F32, (1, T, HV)), "a_log": (kda.KDA_F32, (HV,)),
+        "dt_bias": (kda.KDA_F32, (HV, DK)), "cu_seqlens": (kda.KDA_I32, (B + 1,)),
+        "state_pool": (kda.KDA_F32, (N, HV, DK, DV)), "state_indices": (kda.KDA_I32, (B,)),
+    }
+    return {n: kda.raw_tensor(_FAKE[i], *shapes[n]) for i, n in enumerate(kda.ARG_NAMES)}
+
+
+def call(descs, mode=None, **mode_kw):
+    if mode is None:
+        mode = kda.make_mode(**mode_kw)
+    return kda.call_raw([descs[n] for n in kda.ARG_NAMES], mode, 0)
+
+
+def reshape(desc, shape):
+    return kda.raw_tensor(desc.data, desc.dtype, shape)
+
+
+def test_nothing_to_do_returns_ok_without_launch():
+    d = descriptors(B=0, T=0)
+    assert call(d) == kda.KDA_OK
+    d = descriptors(B=3, T=0)
+    assert call(d) == kda.KDA_OK
+
+
+def test_null_arguments():
+    d = descriptors(B=0, T=0)
+    assert kda.call_raw([d[n] for n in kda.ARG_NAMES], None, 0) == kda.KDA_ERR_NULL
+    for n in kda.ARG_NAMES:
+        e = dict(d)
+        e[n] = None
+        assert call(e) == kda.KDA_ERR_NULL, n
+    d = descriptors()
+    for n in kda.ARG_NAMES:
+        e = dict(d)
+        e[n] = kda.raw_tensor(0, d[n].dtype, tuple(d[n].shape[:d[n].ndim]))
+        assert call(e) == kda.KDA_ERR_NULL, n
+
+
+@pytest.mark.parametrize("name,dtype", [
+    ("q", kda.KDA_F32), ("k", kda.KDA_F32), ("out", kda.KDA_F32), ("v", kda.KDA_I32),
+    ("raw_gate", kda.KDA_BF16), ("beta_logits", kda.KDA_BF16), ("a_log", kda.KDA_I32),
+    ("dt_bias", kda.KDA_BF16), ("state_pool", kda.KDA_BF16), ("cu_seqlens", kda.KDA_F32),
+    ("state_indices", kda.KDA_F32),
+])
+def test_dtype_errors(name, dtype):
+    d = descriptors()
+    d[name] = kda.raw_tensor(d[name].data, dtype, tuple(d[name].shape[:d[name].ndim]))
+    assert call(d) == kda.KDA_ERR_DTYPE
+
+
+def test_shape_errors():
+    base = descriptors()
+    cases = {
+        "q": (2, 3, 2, 128), "k": (1, 3, 2, 64), "v": (1, 4, 4, 128), "out": (1, 3, 4, 64),
+        "raw_gate": (1, 3, 2, 128), "beta_logits": (1, 3, 3), "a_log": (3,),
+        "dt_bias": (4, 64), "cu_seqlens": (4,), "state_pool": (8, 4, 128, 64),
+        "state_indices": (3,),
+    }
+    for name, shape in cases.items():
+        d = dict(base)
+        d[name] = reshape(base[name], shape)
+        assert call(d) == kda.KDA_ERR_SHAPE, name
+    d = dict(base)
+    d["a_log"] = reshape(base["a_log"], (4, 1))           # wrong rank
+    assert call(d) == kda.KDA_ERR_SHAPE
+    d = descriptors(H=3, HV=4)                             # HV % H != 0
+    assert call(d) == kda.KDA_ERR_SHAPE
+    d = dict(base)
+    d["q"] = kda.raw_tensor(base["q"].data, base["q"].dtype, (1, 3, 2, -128))
+    assert call(d) == kda.KDA_ERR_SHAPE
+
+
+@pytest.mark.parametrize("dk,dv", [(48, 128), (128, 96), (256, 128), (128, 8)])
+def test_unsupported_head_dims(dk, dv):
+    assert call(descriptors(DK=dk, DV=dv)) == kda.KDA_ERR_UNSUPPORTED
+
+
+def test_misaligned_pointer_is_unsupported():
+    d = descriptors()
+    d["state_pool"] = kda.raw_tensor(d["state_pool"].data + 4, kda.KDA_F32, (8, 4, 128, 128))
+    assert call(d) == kda.KDA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw", [
+    dict(gate_mode=7),
+    dict(gate_mode="lower_bound", lower_bound=0.5),
+    dict(gate_mode="lower_bound", lower_bound=float("nan")),
+    dict(gate_mode="lower_bound", lower_bound=float("-inf")),
+    dict(l2_eps=-1e-6), dict(l2_eps=float("inf")), dict(l2_eps=float("nan")),
+    dict(scale=-1.0), dict(scale=float("nan")), dict(scale=float("inf")),
+])
+def test_mode_errors(kw):
+    assert call(descriptors(), **kw) == kda.KDA_ERR_MODE
+
+
+def test_python_binding_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    t = torch.zeros(4)
+    with pytest.raises(ValueError):
+        kda.decode(*([t] * 11))
