@@ -23,7 +23,9 @@
 // differs).  The per-channel setup (L2 norms, gate, beta) is computed by the
 // wave itself, two channels per lane, and handed to the row owners through
 // a small LDS table.  The state makes exactly one trip from HBM and one back
-// per call; tokens of the same request keep it in registers.
+// per call; tokens of the same request keep it in registers.  Those two
+// trips carry the nontemporal hint: the tile is touched once per call, and
+// keeping it out of L2 / MALL measurably raises the streaming rate.
 //
 // Workgroup order is XCD-aware: consecutive workgroup ids land on different
 // XCDs, so the id is remapped to give each XCD one contiguous range of
@@ -52,6 +54,29 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
   if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
   u += 0x7fffu + ((u >> 16) & 1u);
   return static_cast<uint16_t>(u >> 16);
+}
+
+// The state is streamed: each tile is read once and written once per call,
+// so its accesses carry the nontemporal hint (cache policy bit "nt") and go
+// through a buffer resource spanning exactly the tile.  The resource keeps
+// the per-row offsets in scalar registers (one VGPR offset per lane) and the
+// hardware range check confines every access to the tile.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+constexpr int kCachePolicyNT = 2;
+constexpr int kRawBufferWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_resource(float* tile, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(tile, static_cast<short>(0), bytes, kRawBufferWord3);
+}
+
+__device__ __forceinline__ float4 load_state(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  const f32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kCachePolicyNT);
+  return make_float4(x.x, x.y, x.z, x.w);
+}
+
+__device__ __forceinline__ void store_state(__amdgpu_buffer_rsrc_t r, int voff, int soff, float4 v) {
+  const f32x4 x = {v.x, v.y, v.z, v.w};
+  __builtin_amdgcn_raw_buffer_store_b128(x, r, voff, soff, kCachePolicyNT);
 }
 
 __device__ __forceinline__ float softplus_f(float x) {
@@ -173,10 +198,12 @@ __global__ __launch_bounds__(kWave) void kda_decode_kernel(const DecodeArgs a) {
 
   // state tile: one trip in
   float* const S_ptr = a.state_pool + (static_cast<int64_t>(slot) * a.HV + hv) * (DK * DV);
+  const __amdgpu_buffer_rsrc_t S_res = tile_resource(S_ptr, DK * DV * 4);
+  const int S_voff = (rs * DV + col0) * 4;
+  constexpr int kRowStep = RS * DV * 4;   // bytes between a lane's rows
   float4 S[R];
 #pragma unroll
-  for (int i = 0; i < R; ++i)
-    S[i] = *reinterpret_cast<const float4*>(S_ptr + (rs + RS * i) * DV + col0);
+  for (int i = 0; i < R; ++i) S[i] = load_state(S_res, S_voff, i * kRowStep);
 
   const bool holds_a = (rs & 4) == 0;          // after the reduction, see below
   const int my_col = col0 + (rs & 3);
@@ -302,8 +329,7 @@ __global__ __launch_bounds__(kWave) void kda_decode_kernel(const DecodeArgs a) {
 
   // state tile: one trip out, to the same slot
 #pragma unroll
-  for (int i = 0; i < R; ++i)
-    *reinterpret_cast<float4*>(S_ptr + (rs + RS * i) * DV + col0) = S[i];
+  for (int i = 0; i < R; ++i) store_state(S_res, S_voff, i * kRowStep, S[i]);
 }
 
 template <int DK, int DV, bool BF16, int GATE>
