@@ -22,7 +22,9 @@
 // into the two reduction vectors (exact algebra; only the rounding order
 // differs).  The per-channel setup (L2 norms, gate, beta) is computed by the
 // wave itself, two channels per lane, and handed to the row owners through
-// a small LDS table.  The state makes exactly one trip from HBM and one back
+// a small LDS table, double-buffered so one token's table never waits for
+// the previous token's readers.  The reductions over the row-group lanes
+// use DPP and the gfx950 row-swap instructions, not LDS round trips.  The state makes exactly one trip from HBM and one back
 // per call; tokens of the same request keep it in registers.  Those two
 // trips carry the nontemporal hint: the tile is touched once per call, and
 // keeping it out of L2 / MALL measurably raises the streaming rate.
@@ -79,18 +81,59 @@ __device__ __forceinline__ void store_state(__amdgpu_buffer_rsrc_t r, int voff, 
   __builtin_amdgcn_raw_buffer_store_b128(x, r, voff, soff, kCachePolicyNT);
 }
 
+// Transcendentals use the hardware exp2 / log2 / rcp / rsqrt instructions
+// (about 1 ulp each).  ln(1 + y) keeps full relative accuracy for small y
+// through the correction of Goldberg, "What every computer scientist should
+// know about floating-point arithmetic" (1991), Theorem 4:
+// ln(1 + y) = y * ln(w) / (w - 1) with w = fl(1 + y), and = y when w == 1.
+__device__ __forceinline__ float exp_f(float x) { return __expf(x); }
+
+__device__ __forceinline__ float log1p_f(float y) {
+  const float w = 1.0f + y;
+  return w == 1.0f ? y : __logf(w) * (y / (w - 1.0f));
+}
+
 __device__ __forceinline__ float softplus_f(float x) {
-  return fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x)));
+  return fmaxf(x, 0.0f) + log1p_f(exp_f(-fabsf(x)));
 }
 
 __device__ __forceinline__ float sigmoid_f(float x) {
-  return 1.0f / (1.0f + expf(-x));
+  return __builtin_amdgcn_rcpf(1.0f + exp_f(-x));
+}
+
+__device__ __forceinline__ float rsqrt_f(float x) { return __builtin_amdgcn_rsqf(x); }
+
+// Cross-lane moves.  DPP reads a neighbour lane inside a 16-lane row;
+// v_permlane16_swap / v_permlane32_swap (gfx950) exchange whole rows.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppSwapPairs = 0xB1;    // quad_perm [1,0,3,2]: lane ^ 1
+constexpr int kDppSwapHalves = 0x4E;   // quad_perm [2,3,0,1]: lane ^ 2
+constexpr int kDppRowRor4 = 0x124;     // lane (i + 4) mod 16 of the row
+constexpr int kDppRowRor8 = 0x128;     // lane (i + 8) mod 16 = lane ^ 8
+
+// Both return keep + the partner's value, where lanes in the lower half of
+// each pair of rows keep `lo` and the upper half keep `hi`:
+//   swap16: rows 16 lanes apart (lane ^ 16); swap32: lane ^ 32.
+__device__ __forceinline__ float swap16_add(float lo, float hi) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(lo), __float_as_uint(hi), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+__device__ __forceinline__ float swap32_add(float lo, float hi) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(lo), __float_as_uint(hi), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) x += __shfl_xor(x, m, kWave);
-  return x;
+  x += dpp<kDppSwapPairs>(x);
+  x += dpp<kDppSwapHalves>(x);
+  x += dpp<kDppRowRor4>(x);
+  x += dpp<kDppRowRor8>(x);
+  x = swap16_add(x, x);
+  return swap32_add(x, x);
 }
 
 // Channels [c0, c0 + CPL) of one token row of q / k (bf16 or f32).
@@ -151,9 +194,11 @@ __global__ __launch_bounds__(kWave) void kda_decode_kernel(const DecodeArgs a) {
   static_assert(DK % RS == 0 && R >= 1, "tile shape");
   static_assert(CPL * kWave >= DK && CPL <= 2, "setup split");
 
-  // per-channel setup table: {kh*alpha, qh*alpha} and {alpha, beta*kh}
-  __shared__ float2 red_tab[DK];
-  __shared__ float2 upd_tab[DK];
+  // per-channel setup tables {kh*alpha, qh*alpha} and {alpha, beta*kh},
+  // double-buffered by token parity, and the slab's u vector
+  __shared__ __attribute__((aligned(16))) float2 red_tab[2][DK];
+  __shared__ __attribute__((aligned(16))) float2 upd_tab[2][DK];
+  __shared__ __attribute__((aligned(16))) float u_tab[CW];
 
   const int lane = threadIdx.x;
   const int cq = lane % CQ;
@@ -194,7 +239,7 @@ __global__ __launch_bounds__(kWave) void kda_decode_kernel(const DecodeArgs a) {
 #pragma unroll
   for (int j = 0; j < CPL; ++j) dtb[j] = 0.0f;
   if (chan_lane) load_f32<CPL>(a.dt_bias + static_cast<int64_t>(hv) * DK + c0, dtb);
-  const float amp = expf(a.a_log[hv]);
+  const float amp = exp_f(a.a_log[hv]);
 
   // state tile: one trip in
   float* const S_ptr = a.state_pool + (static_cast<int64_t>(slot) * a.HV + hv) * (DK * DV);
@@ -208,7 +253,8 @@ __global__ __launch_bounds__(kWave) void kda_decode_kernel(const DecodeArgs a) {
   const bool holds_a = (rs & 4) == 0;          // after the reduction, see below
   const int my_col = col0 + (rs & 3);
 
-  for (int t = t0; t < t1; ++t) {
+  int buf = 0;
+  for (int t = t0; t < t1; ++t, buf ^= 1) {
     // ---- per-token setup: L2 norms, gate, beta (two channels per lane) ----
     float qv[CPL], kv[CPL], xg[CPL];
 #pragma unroll
@@ -233,8 +279,8 @@ __global__ __launch_bounds__(kWave) void kda_decode_kernel(const DecodeArgs a) {
     sq = wave_sum(sq);
     sk = wave_sum(sk);
     sqk = wave_sum(sqk);
-    const float rq = a.scale * rsqrtf(sq + a.l2_eps);
-    const float rk = rsqrtf(sk + a.l2_eps);
+    const float rq = a.scale * rsqrt_f(sq + a.l2_eps);
+    const float rk = rsqrt_f(sk + a.l2_eps);
     const float qk = sqk * rq * rk;             // qh . kh (scale included)
 
     if (chan_lane) {
@@ -244,11 +290,11 @@ __global__ __launch_bounds__(kWave) void kda_decode_kernel(const DecodeArgs a) {
         float g;
         if constexpr (GATE == KDA_GATE_SOFTPLUS) g = -amp * softplus_f(x);
         else g = a.lower_bound * sigmoid_f(amp * x);
-        const float alpha = expf(g);
+        const float alpha = exp_f(g);
         const float kh = kv[j] * rk;
         const float qh = qv[j] * rq;
-        red_tab[c0 + j] = make_float2(kh * alpha, qh * alpha);
-        upd_tab[c0 + j] = make_float2(alpha, beta * kh);
+        red_tab[buf][c0 + j] = make_float2(kh * alpha, qh * alpha);
+        upd_tab[buf][c0 + j] = make_float2(alpha, beta * kh);
       }
     }
     __syncthreads();
@@ -259,7 +305,7 @@ __global__ __launch_bounds__(kWave) void kda_decode_kernel(const DecodeArgs a) {
     for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-      const float2 p = red_tab[rs + RS * i];
+      const float2 p = red_tab[buf][rs + RS * i];
       acc[0] = fmaf(p.x, S[i].x, acc[0]);
       acc[1] = fmaf(p.x, S[i].y, acc[1]);
       acc[2] = fmaf(p.x, S[i].z, acc[2]);
@@ -274,57 +320,64 @@ __global__ __launch_bounds__(kWave) void kda_decode_kernel(const DecodeArgs a) {
     // Lanes of a column group sit CQ apart.  Each butterfly level halves the
     // values a lane carries, so after three levels lane rs holds value
     // rs & 7: a[col0 + (rs&3)] when rs&4 == 0, else b[col0 + (rs&3)].
-    float v4[4];
-    {
-      const bool up = (rs & 4) != 0;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const float send = up ? acc[m] : acc[m + 4];
-        const float keep = up ? acc[m + 4] : acc[m];
-        v4[m] = keep + __shfl_xor(send, 4 * CQ, kWave);
-      }
-    }
-    float v2[2];
-    {
-      const bool up = (rs & 2) != 0;
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const float send = up ? v4[m] : v4[m + 2];
-        const float keep = up ? v4[m + 2] : v4[m];
-        v2[m] = keep + __shfl_xor(send, 2 * CQ, kWave);
-      }
-    }
     float red;
-    {
+    if constexpr (CQ == 8) {
+      // row-group bits are lane bits 5, 4, 3: two row swaps and one DPP move
+      float v4[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) v4[m] = swap32_add(acc[m], acc[m + 4]);
+      float v2[2];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) v2[m] = swap16_add(v4[m], v4[m + 2]);
       const bool up = (rs & 1) != 0;
-      const float send = up ? v2[0] : v2[1];
-      const float keep = up ? v2[1] : v2[0];
-      red = keep + __shfl_xor(send, CQ, kWave);
-    }
+      red = (up ? v2[1] : v2[0]) + dpp<kDppRowRor8>(up ? v2[0] : v2[1]);
+    } else {
+      float v4[4];
+      {
+        const bool up = (rs & 4) != 0;
 #pragma unroll
-    for (int m = 8 * CQ; m < kWave; m <<= 1) red += __shfl_xor(red, m, kWave);
+        for (int m = 0; m < 4; ++m) {
+          const float send = up ? acc[m] : acc[m + 4];
+          const float keep = up ? acc[m + 4] : acc[m];
+          v4[m] = keep + __shfl_xor(send, 4 * CQ, kWave);
+        }
+      }
+      float v2[2];
+      {
+        const bool up = (rs & 2) != 0;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const float send = up ? v4[m] : v4[m + 2];
+          const float keep = up ? v4[m + 2] : v4[m];
+          v2[m] = keep + __shfl_xor(send, 2 * CQ, kWave);
+        }
+      }
+      const bool up = (rs & 1) != 0;
+      red = (up ? v2[1] : v2[0]) + __shfl_xor(up ? v2[0] : v2[1], CQ, kWave);
+#pragma unroll
+      for (int m = 8 * CQ; m < kWave; m <<= 1) red += __shfl_xor(red, m, kWave);
+    }
 
-    // ---- u = v - a; o = b + beta*(qh.kh)*u ----
-    const float u_mine = v_mine - red;                       // meaningful where holds_a
-    const float u_pair = __shfl_xor(u_mine, 4 * CQ, kWave);  // the a-lane of my column
+    // ---- u = v - a (to every lane of the column group); o = b + beta*(qh.kh)*u ----
+    if (holds_a && rs < 4) u_tab[4 * cq + rs] = v_mine - red;
+    __syncthreads();
+    const float4 u4 = *reinterpret_cast<const float4*>(&u_tab[4 * cq]);
     if (!holds_a && rs < 8) {
-      const float o = fmaf(beta * qk, u_pair, red);
-      store_scalar<BF16>(a.out, (static_cast<int64_t>(t) * a.HV + hv) * DV + my_col, o);
+      const float uj = (rs & 2) ? ((rs & 1) ? u4.w : u4.z) : ((rs & 1) ? u4.y : u4.x);
+      store_scalar<BF16>(a.out, (static_cast<int64_t>(t) * a.HV + hv) * DV + my_col,
+                         fmaf(beta * qk, uj, red));
     }
-    float u[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) u[j] = __shfl(u_mine, j * CQ + cq, kWave);
+    const float u[4] = {u4.x, u4.y, u4.z, u4.w};
 
     // ---- S = alpha*S + (beta*kh) u^T ----
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-      const float2 p = upd_tab[rs + RS * i];
+      const float2 p = upd_tab[buf][rs + RS * i];
       S[i].x = fmaf(p.y, u[0], p.x * S[i].x);
       S[i].y = fmaf(p.y, u[1], p.x * S[i].y);
       S[i].z = fmaf(p.y, u[2], p.x * S[i].z);
       S[i].w = fmaf(p.y, u[3], p.x * S[i].w);
     }
-    __syncthreads();   // the tables are rewritten by the next token
   }
 
   // state tile: one trip out, to the same slot
