@@ -75,7 +75,7 @@ def cpu_baseline(inp, pool_t, budget_s: float):
     def gather_tiles(slots, hvs):
         s = torch.as_tensor(slots, dtype=torch.int64, device=pool_t.device)
         h = torch.as_tensor(hvs, dtype=torch.int64, device=pool_t.device)
-        return pool_t[s, h].cpu().numpy()
+        return pool_t[s, h].float().cpu().numpy()
 
     cfg = inp.cfg
     lb = cfg.lower_bound if cfg.gate_mode == "lower_bound" else None
@@ -94,12 +94,13 @@ def cpu_baseline(inp, pool_t, budget_s: float):
             t0 = time.perf_counter()
             ko.kda_decode(inp.q, inp.k, inp.v, inp.raw_gate, inp.beta_logits, inp.a_log,
                           inp.dt_bias, inp.cu_seqlens, pool, inp.state_indices, tiles=tiles,
-                          gate_mode=cfg.gate_mode, lower_bound=lb)
+                          gate_mode=cfg.gate_mode, lower_bound=lb, state_layout=cfg.state_layout,
+                          state_dtype=cfg.state_dtype)
             elapsed += time.perf_counter() - t0
             counts = np.diff(inp.cu_seqlens[b:b + step + 1])
             done_th += int(counts.sum()) * cfg.HV
             done_state += int(((counts > 0) & (inp.state_indices[b:b + step] >= 0)).sum()) \
-                * cfg.HV * 2 * cfg.DK * cfg.DV * 4
+                * cfg.HV * 2 * cfg.DK * cfg.DV * cfg.state_elem_bytes
             done_req += step
             b += step
     return {
@@ -148,6 +149,8 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None)
+    ap.add_argument("--state-layout", choices=("k_first", "v_first"), default="k_first")
+    ap.add_argument("--state-dtype", choices=("f32", "bf16"), default="f32")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for cpu_baseline (0 disables)")
     ap.add_argument("--no-copy-ceiling", action="store_true")
@@ -170,7 +173,7 @@ def main(argv=None) -> int:
     kda.library()     # fail loudly if the HIP library is not built
 
     name = args.workload or wl.HEADLINE
-    cfg = wl.PRESETS[name]
+    cfg = wl.preset(name, state_layout=args.state_layout, state_dtype=args.state_dtype)
     log(f"[bench] workload {name}: {cfg.description}")
     inp = wl.draw(cfg)
     dev = wl.to_device(inp)
@@ -184,7 +187,7 @@ def main(argv=None) -> int:
 
     stream = torch.cuda.current_stream()
     handle = stream.cuda_stream
-    mode = dict(gate_mode=cfg.gate_mode, lower_bound=cfg.lower_bound)
+    mode = dict(gate_mode=cfg.gate_mode, lower_bound=cfg.lower_bound, state_layout=cfg.state_layout)
 
     def step():
         kda.decode(out, dev["q"], dev["k"], dev["v"], dev["raw_gate"], dev["beta_logits"],
@@ -214,7 +217,9 @@ def main(argv=None) -> int:
 
     value = state_b / (ms_per_step * 1e-3) / 1e9
     achieved = alg_bytes / (mean_kernel_ms * 1e-3) / 1e9
-    traffic, traffic_src = committed_traffic(name)
+    variant = "" if (cfg.state_layout, cfg.state_dtype) == ("k_first", "f32") else \
+        f"_{cfg.state_layout}_{cfg.state_dtype}"
+    traffic, traffic_src = committed_traffic(name + variant)
     log(f"[bench] traffic: {traffic} ({traffic_src})")
 
     copy_gbps = None
@@ -246,7 +251,8 @@ def main(argv=None) -> int:
         "config": {
             "workload": name, "B": cfg.B, "H": cfg.H, "HV": cfg.HV, "dk": cfg.DK, "dv": cfg.DV,
             "tokens_per_request": cfg.tokens, "total_tokens": inp.T,
-            "qkv_dtype": cfg.qkv_dtype, "state_dtype": "f32", "gate": cfg.gate_mode,
+            "qkv_dtype": cfg.qkv_dtype, "state_dtype": cfg.state_dtype,
+            "state_layout": cfg.state_layout, "gate": cfg.gate_mode,
             "slots": cfg.n_slots, "parallelism": "single GPU",
         },
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
@@ -263,7 +269,8 @@ def main(argv=None) -> int:
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "kernel": "kda_decode_kernel<128,128,bf16,%s>" % cfg.gate_mode,
+            "kernel": "kda_decode_%s<%d,%d,%s q/k/v,%s state>" % (
+                cfg.state_layout.replace("_", ""), cfg.DK, cfg.DV, cfg.qkv_dtype, cfg.state_dtype),
         },
         "cpu_baseline": cpu,
         "active_tiles": int(((counts > 0) & (inp.state_indices >= 0)).sum()) * cfg.HV,

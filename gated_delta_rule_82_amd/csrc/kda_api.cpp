@@ -4,7 +4,8 @@
 // a bad call returns its error code without touching the device.  The
 // tensor contract is the one of the "KdaDecode" page (Tensor Shapes): packed
 // [1, total_T, ...] token tensors, [HV] / [HV, dk] gate parameters, int32
-// cu_seqlens and state_indices, and a [max_slots, HV, dk, dv] fp32 pool.
+// cu_seqlens and state_indices, and a [max_slots, HV, dk, dv] state pool
+// (key-first, or its value-first transpose; f32 or bf16).
 
 #include <cmath>
 #include <cstdint>
@@ -57,7 +58,7 @@ const char* kda_status_string(int status) {
     case KDA_ERR_DTYPE: return "a tensor has an unsupported or mismatched dtype";
     case KDA_ERR_SHAPE: return "tensor ranks or extents disagree";
     case KDA_ERR_UNSUPPORTED: return "head size not in {16, 32, 64, 128}, misaligned data, or size too large";
-    case KDA_ERR_MODE: return "invalid gate mode, lower_bound, l2_eps or scale";
+    case KDA_ERR_MODE: return "invalid gate mode, lower_bound, l2_eps, scale or state layout";
     case KDA_ERR_LAUNCH: return "the HIP kernel launch failed";
     case KDA_ERR_PRECONDITION: return "cu_seqlens or state_indices violate their preconditions";
     default: return "unknown status";
@@ -106,8 +107,9 @@ int kda_decode(const kda_tensor* out, const kda_tensor* q, const kda_tensor* k,
   if (qkv != KDA_BF16 && qkv != KDA_F32) return KDA_ERR_DTYPE;
   if (q->dtype != qkv || k->dtype != qkv || out->dtype != qkv) return KDA_ERR_DTYPE;
   if (raw_gate->dtype != KDA_F32 || beta_logits->dtype != KDA_F32 || a_log->dtype != KDA_F32 ||
-      dt_bias->dtype != KDA_F32 || state_pool->dtype != KDA_F32)
+      dt_bias->dtype != KDA_F32)
     return KDA_ERR_DTYPE;
+  if (state_pool->dtype != KDA_F32 && state_pool->dtype != KDA_BF16) return KDA_ERR_DTYPE;
   if (cu_seqlens->dtype != KDA_I32 || state_indices->dtype != KDA_I32) return KDA_ERR_DTYPE;
 
   // extents
@@ -127,7 +129,11 @@ int kda_decode(const kda_tensor* out, const kda_tensor* q, const kda_tensor* k,
   if (a_log->shape[0] != HV || dt_bias->shape[0] != HV || dt_bias->shape[1] != DK)
     return KDA_ERR_SHAPE;
   if (cu_seqlens->shape[0] != B + 1) return KDA_ERR_SHAPE;
-  if (state_pool->shape[1] != HV || state_pool->shape[2] != DK || state_pool->shape[3] != DV)
+  if (mode->state_layout != KDA_STATE_K_FIRST && mode->state_layout != KDA_STATE_V_FIRST)
+    return KDA_ERR_MODE;
+  const bool v_first = mode->state_layout == KDA_STATE_V_FIRST;
+  if (state_pool->shape[1] != HV || state_pool->shape[2] != (v_first ? DV : DK) ||
+      state_pool->shape[3] != (v_first ? DK : DV))
     return KDA_ERR_SHAPE;
   if (H < 1 || HV < 1 || HV % H != 0) return KDA_ERR_SHAPE;
 
@@ -163,7 +169,7 @@ int kda_decode(const kda_tensor* out, const kda_tensor* q, const kda_tensor* k,
   args.a_log = static_cast<const float*>(a_log->data);
   args.dt_bias = static_cast<const float*>(dt_bias->data);
   args.cu_seqlens = static_cast<const int32_t*>(cu_seqlens->data);
-  args.state_pool = static_cast<float*>(state_pool->data);
+  args.state_pool = state_pool->data;
   args.state_indices = static_cast<const int32_t*>(state_indices->data);
   args.B = static_cast<int32_t>(B);
   args.T = static_cast<int32_t>(T);
@@ -171,11 +177,12 @@ int kda_decode(const kda_tensor* out, const kda_tensor* q, const kda_tensor* k,
   args.HV = static_cast<int32_t>(HV);
   args.G = static_cast<int32_t>(HV / H);
   args.N = static_cast<int32_t>(N);
+  args.gate_mode = mode->gate_mode;
   args.lower_bound = mode->gate_mode == KDA_GATE_LOWER_BOUND ? mode->lower_bound : 0.0f;
   args.l2_eps = mode->l2_eps == 0.0f ? 1e-6f : mode->l2_eps;
   args.scale = mode->scale == 0.0f ? 1.0f / std::sqrt(static_cast<float>(DK)) : mode->scale;
   return kda::launch_decode(args, static_cast<int>(DK), static_cast<int>(DV), qkv == KDA_BF16,
-                            mode->gate_mode, stream);
+                            state_pool->dtype == KDA_BF16, mode->state_layout, stream);
 }
 
 }  // extern "C"

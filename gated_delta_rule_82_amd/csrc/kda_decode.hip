@@ -1,19 +1,24 @@
 // kda_decode.hip - the KDA decode recurrence for CDNA4 (gfx950).
 //
 // Operation ("Delta-rule write" page, naive_recurrent_kda code excerpt;
-// "KdaDecode" Tensor Shapes; "KDA Block TKG" l2_eps / scale / lower_bound):
-// per token, decay the key-first state row k by exp(g[k]), write
-// (beta*k) outer (v - k^T S), and read o = q^T S from the updated state.
+// "KdaDecode" Tensor Shapes and default parameters; "KDA Block TKG"
+// l2_eps / scale / lower_bound): per token, decay state row k by
+// exp(g[k]), write (beta*k) outer (v - k^T S), and read o = q^T S from the
+// updated state.
 //
-// Work decomposition.  The columns of a state tile never interact: column c
-// of S only meets v[c] and o[c]; every reduction runs over the key axis.  So
-// one wavefront owns a 32-column slab (all dk rows) of one (request, value
-// head) tile and needs no other wave: no cross-wave reduction and no
-// workgroup barrier.  A workgroup is that one wave.  Lane (rs, cq) of the
-// wave holds rows rs + RS*i (i < R) and columns 4cq..4cq+3 of the slab as R
-// float4 registers, so each load instruction of the wave reads RS whole
-// 128-byte row segments; for dk = dv = 128 that is 16 x 128-bit loads per
-// lane and 64 VGPRs of state.
+// Work decomposition.  The value columns of a state tile never interact:
+// column v of S only meets v[v] and o[v]; every reduction runs over the key
+// axis.  So one wavefront owns a 32-value slab of one (request, value head)
+// tile for all dk keys and needs no other wave: no cross-wave reduction and
+// no workgroup barrier.  A workgroup is that one wave.  How the slab maps to
+// lanes depends on the state layout:
+//   key-first [dk][dv]  ("K_FIRST", the default): lane (rs, cq) holds keys
+//       rs + RS*i and values 4cq..4cq+3; each load instruction of the wave
+//       reads RS rows of 128 bytes (32 fp32 values);
+//   value-first [dv][dk] (the transposed layout the model asks for): lane
+//       (rsub, kc) holds value rows rsub + RPI*i and keys 4kc..4kc+3; each
+//       load instruction reads RPI whole rows, one contiguous KiB.
+// For dk = dv = 128 a lane carries 64 fp32 state values in VGPRs.
 //
 // Per token, with alpha = exp(g):
 //   a = (kh*alpha)^T S_old,  b = (qh*alpha)^T S_old      (one sweep over S)
@@ -21,13 +26,16 @@
 // which is the page's decay / write / read sequence with the decay folded
 // into the two reduction vectors (exact algebra; only the rounding order
 // differs).  The per-channel setup (L2 norms, gate, beta) is computed by the
-// wave itself, two channels per lane, and handed to the row owners through
-// a small LDS table, double-buffered so one token's table never waits for
-// the previous token's readers.  The reductions over the row-group lanes
-// use DPP and the gfx950 row-swap instructions, not LDS round trips.  The state makes exactly one trip from HBM and one back
-// per call; tokens of the same request keep it in registers.  Those two
-// trips carry the nontemporal hint: the tile is touched once per call, and
-// keeping it out of L2 / MALL measurably raises the streaming rate.
+// wave itself, two channels per lane, and handed to the lanes that need it
+// through a small LDS table, double-buffered so one token's table never
+// waits for the previous token's readers.  The reductions over lanes use DPP
+// and the gfx950 row-swap instructions where the lane pattern allows.
+//
+// The state makes exactly one trip from HBM and one back per call; tokens
+// of the same request keep it in registers (fp32 even for a bf16 pool, which
+// is rounded to nearest-even once, on the way out).  Both trips carry the
+// nontemporal hint: the tile is touched once per call, and keeping it out of
+// L2 / MALL measurably raises the streaming rate.
 //
 // Workgroup order is XCD-aware: consecutive workgroup ids land on different
 // XCDs, so the id is remapped to give each XCD one contiguous range of
@@ -46,39 +54,20 @@ namespace {
 constexpr int kWave = 64;
 constexpr int kXcds = 8;
 
+// ---------------------------------------------------------------------------
+// numbers
+// ---------------------------------------------------------------------------
+
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
 
 // fp32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
   uint32_t u = __float_as_uint(x);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
   u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
-}
-
-// The state is streamed: each tile is read once and written once per call,
-// so its accesses carry the nontemporal hint (cache policy bit "nt") and go
-// through a buffer resource spanning exactly the tile.  The resource keeps
-// the per-row offsets in scalar registers (one VGPR offset per lane) and the
-// hardware range check confines every access to the tile.
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-constexpr int kCachePolicyNT = 2;
-constexpr int kRawBufferWord3 = 0x00020000;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_resource(float* tile, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(tile, static_cast<short>(0), bytes, kRawBufferWord3);
-}
-
-__device__ __forceinline__ float4 load_state(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-  const f32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kCachePolicyNT);
-  return make_float4(x.x, x.y, x.z, x.w);
-}
-
-__device__ __forceinline__ void store_state(__amdgpu_buffer_rsrc_t r, int voff, int soff, float4 v) {
-  const f32x4 x = {v.x, v.y, v.z, v.w};
-  __builtin_amdgcn_raw_buffer_store_b128(x, r, voff, soff, kCachePolicyNT);
+  return u >> 16;
 }
 
 // Transcendentals use the hardware exp2 / log2 / rcp / rsqrt instructions
@@ -103,20 +92,30 @@ __device__ __forceinline__ float sigmoid_f(float x) {
 
 __device__ __forceinline__ float rsqrt_f(float x) { return __builtin_amdgcn_rsqf(x); }
 
-// Cross-lane moves.  DPP reads a neighbour lane inside a 16-lane row;
-// v_permlane16_swap / v_permlane32_swap (gfx950) exchange whole rows.
+// ---------------------------------------------------------------------------
+// cross-lane moves: DPP reads a neighbour lane inside a 16-lane row;
+// v_permlane16_swap / v_permlane32_swap (gfx950) exchange whole rows
+// ---------------------------------------------------------------------------
+
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
 }
-constexpr int kDppSwapPairs = 0xB1;    // quad_perm [1,0,3,2]: lane ^ 1
-constexpr int kDppSwapHalves = 0x4E;   // quad_perm [2,3,0,1]: lane ^ 2
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppQuadReverse = 0x1B;  // quad_perm [3,2,1,0]: lane ^ 3
+constexpr int kDppHalfMirror = 0x141;  // lane 7 - i within each group of 8
 constexpr int kDppRowRor4 = 0x124;     // lane (i + 4) mod 16 of the row
 constexpr int kDppRowRor8 = 0x128;     // lane (i + 8) mod 16 = lane ^ 8
 
+// lane ^ 4: the half-row mirror (7 - i) read through the quad reversal (i ^ 3)
+__device__ __forceinline__ float dpp_xor4(float x) {
+  return dpp<kDppQuadReverse>(dpp<kDppHalfMirror>(x));
+}
+
 // Both return keep + the partner's value, where lanes in the lower half of
 // each pair of rows keep `lo` and the upper half keep `hi`:
-//   swap16: rows 16 lanes apart (lane ^ 16); swap32: lane ^ 32.
+//   swap16: partner lane ^ 16; swap32: partner lane ^ 32.
 __device__ __forceinline__ float swap16_add(float lo, float hi) {
   const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(lo), __float_as_uint(hi), false, false);
   return __uint_as_float(p[0]) + __uint_as_float(p[1]);
@@ -127,14 +126,71 @@ __device__ __forceinline__ float swap32_add(float lo, float hi) {
   return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
+// One transpose-reduce level through a within-row DPP move: lanes whose
+// level bit is clear (up == false) keep `lo` and receive the partner's `lo`,
+// the others keep `hi` and receive the partner's `hi`.
+template <int XOR>
+__device__ __forceinline__ float dpp_level(bool up, float lo, float hi) {
+  const float send = up ? lo : hi;
+  const float keep = up ? hi : lo;
+  if constexpr (XOR == 1) return keep + dpp<kDppXor1>(send);
+  else if constexpr (XOR == 2) return keep + dpp<kDppXor2>(send);
+  else if constexpr (XOR == 4) return keep + dpp_xor4(send);
+  else return keep + dpp<kDppRowRor8>(send);
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
-  x += dpp<kDppSwapPairs>(x);
-  x += dpp<kDppSwapHalves>(x);
+  x += dpp<kDppXor1>(x);
+  x += dpp<kDppXor2>(x);
   x += dpp<kDppRowRor4>(x);
   x += dpp<kDppRowRor8>(x);
   x = swap16_add(x, x);
   return swap32_add(x, x);
 }
+
+// ---------------------------------------------------------------------------
+// memory
+// ---------------------------------------------------------------------------
+
+// The state is streamed through a raw buffer resource spanning exactly the
+// tile: per-row offsets stay in scalar registers (one VGPR offset per lane),
+// the hardware range check confines every access to the tile, and the
+// cache-policy bit "nt" marks the data as touched once.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+constexpr int kCachePolicyNT = 2;
+constexpr int kRawBufferWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_resource(void* tile, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(tile, static_cast<short>(0), bytes, kRawBufferWord3);
+}
+
+// Four consecutive state elements of one row: fp32 (16 bytes) or bf16
+// (8 bytes, rounded to nearest-even on the way out).
+template <bool SBF16>
+struct StateIO {
+  static constexpr int kElem = SBF16 ? 2 : 4;
+  __device__ static __forceinline__ float4 load(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    if constexpr (SBF16) {
+      const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kCachePolicyNT);
+      return make_float4(bf16_to_f32(w.x & 0xffffu), __uint_as_float(w.x & 0xffff0000u),
+                         bf16_to_f32(w.y & 0xffffu), __uint_as_float(w.y & 0xffff0000u));
+    } else {
+      const f32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kCachePolicyNT);
+      return make_float4(x.x, x.y, x.z, x.w);
+    }
+  }
+  __device__ static __forceinline__ void store(__amdgpu_buffer_rsrc_t r, int voff, int soff, float4 v) {
+    if constexpr (SBF16) {
+      const u32x2 w = {f32_to_bf16_rne(v.x) | (f32_to_bf16_rne(v.y) << 16),
+                       f32_to_bf16_rne(v.z) | (f32_to_bf16_rne(v.w) << 16)};
+      __builtin_amdgcn_raw_buffer_store_b64(w, r, voff, soff, kCachePolicyNT);
+    } else {
+      const f32x4 x = {v.x, v.y, v.z, v.w};
+      __builtin_amdgcn_raw_buffer_store_b128(x, r, voff, soff, kCachePolicyNT);
+    }
+  }
+};
 
 // Channels [c0, c0 + CPL) of one token row of q / k (bf16 or f32).
 template <bool BF16, int CPL>
@@ -142,7 +198,7 @@ __device__ __forceinline__ void load_qk(const void* base, int64_t off, float (&x
   if constexpr (BF16) {
     const uint16_t* p = static_cast<const uint16_t*>(base) + off;
     if constexpr (CPL == 2) {
-      uint32_t w = *reinterpret_cast<const uint32_t*>(p);
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
       x[0] = bf16_to_f32(w & 0xffffu);
       x[1] = __uint_as_float(w & 0xffff0000u);
     } else {
@@ -151,7 +207,7 @@ __device__ __forceinline__ void load_qk(const void* base, int64_t off, float (&x
   } else {
     const float* p = static_cast<const float*>(base) + off;
     if constexpr (CPL == 2) {
-      float2 w = *reinterpret_cast<const float2*>(p);
+      const float2 w = *reinterpret_cast<const float2*>(p);
       x[0] = w.x;
       x[1] = w.y;
     } else {
@@ -163,7 +219,7 @@ __device__ __forceinline__ void load_qk(const void* base, int64_t off, float (&x
 template <int CPL>
 __device__ __forceinline__ void load_f32(const float* p, float (&x)[CPL]) {
   if constexpr (CPL == 2) {
-    float2 w = *reinterpret_cast<const float2*>(p);
+    const float2 w = *reinterpret_cast<const float2*>(p);
     x[0] = w.x;
     x[1] = w.y;
   } else {
@@ -179,31 +235,21 @@ __device__ __forceinline__ float load_scalar(const void* base, int64_t off) {
 
 template <bool BF16>
 __device__ __forceinline__ void store_scalar(void* base, int64_t off, float x) {
-  if constexpr (BF16) static_cast<uint16_t*>(base)[off] = f32_to_bf16_rne(x);
+  if constexpr (BF16) static_cast<uint16_t*>(base)[off] = static_cast<uint16_t>(f32_to_bf16_rne(x));
   else static_cast<float*>(base)[off] = x;
 }
 
-template <int DK, int DV, bool BF16, int GATE>
-__global__ __launch_bounds__(kWave) void kda_decode_kernel(const DecodeArgs a) {
-  constexpr int CW = DV < 32 ? DV : 32;   // columns of the wave's slab
-  constexpr int SLABS = DV / CW;
-  constexpr int CQ = CW / 4;              // float4 column groups per slab
-  constexpr int RS = kWave / CQ;          // row groups across the wave
-  constexpr int R = DK / RS;              // rows per lane
-  constexpr int CPL = DK >= 2 * kWave ? DK / kWave : 1;   // setup channels per lane
-  static_assert(DK % RS == 0 && R >= 1, "tile shape");
-  static_assert(CPL * kWave >= DK && CPL <= 2, "setup split");
+// ---------------------------------------------------------------------------
+// the pieces both layouts share
+// ---------------------------------------------------------------------------
 
-  // per-channel setup tables {kh*alpha, qh*alpha} and {alpha, beta*kh},
-  // double-buffered by token parity, and the slab's u vector
-  __shared__ __attribute__((aligned(16))) float2 red_tab[2][DK];
-  __shared__ __attribute__((aligned(16))) float2 upd_tab[2][DK];
-  __shared__ __attribute__((aligned(16))) float u_tab[CW];
+// Which tile and slab this workgroup owns, and the request's token range.
+struct TileJob {
+  int b, hv, h, slab, t0, t1, slot;
+};
 
-  const int lane = threadIdx.x;
-  const int cq = lane % CQ;
-  const int rs = lane / CQ;
-
+template <int SLABS>
+__device__ __forceinline__ TileJob resolve_job(const DecodeArgs& a) {
   // XCD-aware id -> (tile, slab)
   const uint32_t wg = blockIdx.x;
   const uint32_t nwg = gridDim.x;
@@ -211,98 +257,143 @@ __global__ __launch_bounds__(kWave) void kda_decode_kernel(const DecodeArgs a) {
   const uint32_t per = nwg / kXcds;
   const uint32_t extra = nwg % kXcds;
   const uint32_t logical = xcd * per + (xcd < extra ? xcd : extra) + wg / kXcds;
-  const int slab = static_cast<int>(logical % SLABS);
+  TileJob j;
+  j.slab = static_cast<int>(logical % SLABS);
   const int tile = static_cast<int>(logical / SLABS);
-  const int b = tile / a.HV;
-  const int hv = tile - b * a.HV;
-  const int h = hv / a.G;
-
-  int t0 = a.cu_seqlens[b];
-  int t1 = a.cu_seqlens[b + 1];
+  j.b = tile / a.HV;
+  j.hv = tile - j.b * a.HV;
+  j.h = j.hv / a.G;
+  int t0 = a.cu_seqlens[j.b];
+  int t1 = a.cu_seqlens[j.b + 1];
   t0 = t0 < 0 ? 0 : (t0 > a.T ? a.T : t0);
   t1 = t1 < t0 ? t0 : (t1 > a.T ? a.T : t1);
-  const int slot = a.state_indices[b];
-  const int col0 = slab * CW + 4 * cq;
+  j.t0 = t0;
+  j.t1 = t1;
+  j.slot = a.state_indices[j.b];
+  return j;
+}
 
-  if (slot < 0 || slot >= a.N) {
-    // skipped request: zero its output rows, leave every slot alone
-    for (int t = t0; t < t1; ++t)
-      if (lane < CW) store_scalar<BF16>(a.out, (static_cast<int64_t>(t) * a.HV + hv) * DV + slab * CW + lane, 0.0f);
+// Skipped request: zero its output rows in this slab, leave every slot alone.
+template <int DV, int CW, bool BF16>
+__device__ __forceinline__ void zero_rows(const DecodeArgs& a, const TileJob& j, int lane) {
+  for (int t = j.t0; t < j.t1; ++t)
+    if (lane < CW) store_scalar<BF16>(a.out, (static_cast<int64_t>(t) * a.HV + j.hv) * DV + j.slab * CW + lane, 0.0f);
+}
+
+struct TokenScalars {
+  float beta;   // write strength
+  float qk;     // qh . kh, query scale included
+};
+
+// Per-token setup, CPL channels per lane: L2 norms (wave reductions), gate,
+// beta; fills red_tab[c] = {kh*alpha, qh*alpha} and upd_tab[c] = {alpha,
+// beta*kh} for the wave's channels.
+template <int DK, int CPL, bool QBF16>
+__device__ __forceinline__ TokenScalars token_setup(const DecodeArgs& a, const TileJob& j, int t, int c0,
+                                                    bool chan_lane, const float (&dtb)[CPL], float amp,
+                                                    float2* red_tab, float2* upd_tab) {
+  float qv[CPL], kv[CPL], xg[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) qv[c] = kv[c] = xg[c] = 0.0f;
+  if (chan_lane) {
+    const int64_t qk_off = (static_cast<int64_t>(t) * a.H + j.h) * DK + c0;
+    load_qk<QBF16, CPL>(a.q, qk_off, qv);
+    load_qk<QBF16, CPL>(a.k, qk_off, kv);
+    load_f32<CPL>(a.raw_gate + (static_cast<int64_t>(t) * a.HV + j.hv) * DK + c0, xg);
+  }
+  TokenScalars s;
+  s.beta = sigmoid_f(a.beta_logits[static_cast<int64_t>(t) * a.HV + j.hv]);
+  float sq = 0.0f, sk = 0.0f, sqk = 0.0f;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    sq = fmaf(qv[c], qv[c], sq);
+    sk = fmaf(kv[c], kv[c], sk);
+    sqk = fmaf(qv[c], kv[c], sqk);
+  }
+  sq = wave_sum(sq);
+  sk = wave_sum(sk);
+  sqk = wave_sum(sqk);
+  const float rq = a.scale * rsqrt_f(sq + a.l2_eps);
+  const float rk = rsqrt_f(sk + a.l2_eps);
+  s.qk = sqk * rq * rk;
+  if (chan_lane) {
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const float x = xg[c] + dtb[c];
+      const float g = a.gate_mode == KDA_GATE_SOFTPLUS ? -amp * softplus_f(x)
+                                                       : a.lower_bound * sigmoid_f(amp * x);
+      const float alpha = exp_f(g);
+      const float kh = kv[c] * rk;
+      const float qh = qv[c] * rq;
+      red_tab[c0 + c] = make_float2(kh * alpha, qh * alpha);
+      upd_tab[c0 + c] = make_float2(alpha, s.beta * kh);
+    }
+  }
+  return s;
+}
+
+// ---------------------------------------------------------------------------
+// key-first layout: state [dk][dv]
+// ---------------------------------------------------------------------------
+
+template <int DK, int DV, bool QBF16, bool SBF16>
+__global__ __launch_bounds__(kWave) void kda_decode_kfirst(const DecodeArgs a) {
+  constexpr int CW = DV < 32 ? DV : 32;   // value columns of the wave's slab
+  constexpr int SLABS = DV / CW;
+  constexpr int CQ = CW / 4;              // float4 column groups per slab
+  constexpr int RS = kWave / CQ;          // row groups across the wave
+  constexpr int R = DK / RS;              // rows per lane
+  constexpr int CPL = DK >= 2 * kWave ? DK / kWave : 1;   // setup channels per lane
+  static_assert(DK % RS == 0 && R >= 1, "tile shape");
+  static_assert(CPL * kWave >= DK && CPL <= 2, "setup split");
+  using IO = StateIO<SBF16>;
+
+  __shared__ __attribute__((aligned(16))) float2 red_tab[2][DK];
+  __shared__ __attribute__((aligned(16))) float2 upd_tab[2][DK];
+  __shared__ __attribute__((aligned(16))) float u_tab[CW];
+
+  const int lane = threadIdx.x;
+  const int cq = lane % CQ;
+  const int rs = lane / CQ;
+  const TileJob j = resolve_job<SLABS>(a);
+  if (j.slot < 0 || j.slot >= a.N) {
+    zero_rows<DV, CW, QBF16>(a, j, lane);
     return;
   }
-  if (t0 == t1) return;
+  if (j.t0 == j.t1) return;
 
-  // token-invariant per-head parameters
+  const int col0 = j.slab * CW + 4 * cq;
   const int c0 = lane * CPL;
   const bool chan_lane = c0 < DK;
   float dtb[CPL];
 #pragma unroll
-  for (int j = 0; j < CPL; ++j) dtb[j] = 0.0f;
-  if (chan_lane) load_f32<CPL>(a.dt_bias + static_cast<int64_t>(hv) * DK + c0, dtb);
-  const float amp = exp_f(a.a_log[hv]);
+  for (int c = 0; c < CPL; ++c) dtb[c] = 0.0f;
+  if (chan_lane) load_f32<CPL>(a.dt_bias + static_cast<int64_t>(j.hv) * DK + c0, dtb);
+  const float amp = exp_f(a.a_log[j.hv]);
 
   // state tile: one trip in
-  float* const S_ptr = a.state_pool + (static_cast<int64_t>(slot) * a.HV + hv) * (DK * DV);
-  const __amdgpu_buffer_rsrc_t S_res = tile_resource(S_ptr, DK * DV * 4);
-  const int S_voff = (rs * DV + col0) * 4;
-  constexpr int kRowStep = RS * DV * 4;   // bytes between a lane's rows
+  char* const tile = static_cast<char*>(a.state_pool) +
+                     (static_cast<int64_t>(j.slot) * a.HV + j.hv) * (DK * DV * IO::kElem);
+  const __amdgpu_buffer_rsrc_t res = tile_resource(tile, DK * DV * IO::kElem);
+  const int voff = (rs * DV + col0) * IO::kElem;
+  constexpr int kRowStep = RS * DV * IO::kElem;   // bytes between a lane's rows
   float4 S[R];
 #pragma unroll
-  for (int i = 0; i < R; ++i) S[i] = load_state(S_res, S_voff, i * kRowStep);
+  for (int i = 0; i < R; ++i) S[i] = IO::load(res, voff, i * kRowStep);
 
   const bool holds_a = (rs & 4) == 0;          // after the reduction, see below
   const int my_col = col0 + (rs & 3);
 
   int buf = 0;
-  for (int t = t0; t < t1; ++t, buf ^= 1) {
-    // ---- per-token setup: L2 norms, gate, beta (two channels per lane) ----
-    float qv[CPL], kv[CPL], xg[CPL];
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) qv[j] = kv[j] = xg[j] = 0.0f;
-    const int64_t qk_off = (static_cast<int64_t>(t) * a.H + h) * DK + c0;
-    const int64_t g_off = (static_cast<int64_t>(t) * a.HV + hv) * DK + c0;
-    if (chan_lane) {
-      load_qk<BF16, CPL>(a.q, qk_off, qv);
-      load_qk<BF16, CPL>(a.k, qk_off, kv);
-      load_f32<CPL>(a.raw_gate + g_off, xg);
-    }
-    const float beta = sigmoid_f(a.beta_logits[static_cast<int64_t>(t) * a.HV + hv]);
-    const float v_mine = holds_a ? load_scalar<BF16>(a.v, (static_cast<int64_t>(t) * a.HV + hv) * DV + my_col) : 0.0f;
-
-    float sq = 0.0f, sk = 0.0f, sqk = 0.0f;
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      sq = fmaf(qv[j], qv[j], sq);
-      sk = fmaf(kv[j], kv[j], sk);
-      sqk = fmaf(qv[j], kv[j], sqk);
-    }
-    sq = wave_sum(sq);
-    sk = wave_sum(sk);
-    sqk = wave_sum(sqk);
-    const float rq = a.scale * rsqrt_f(sq + a.l2_eps);
-    const float rk = rsqrt_f(sk + a.l2_eps);
-    const float qk = sqk * rq * rk;             // qh . kh (scale included)
-
-    if (chan_lane) {
-#pragma unroll
-      for (int j = 0; j < CPL; ++j) {
-        const float x = xg[j] + dtb[j];
-        float g;
-        if constexpr (GATE == KDA_GATE_SOFTPLUS) g = -amp * softplus_f(x);
-        else g = a.lower_bound * sigmoid_f(amp * x);
-        const float alpha = exp_f(g);
-        const float kh = kv[j] * rk;
-        const float qh = qv[j] * rq;
-        red_tab[buf][c0 + j] = make_float2(kh * alpha, qh * alpha);
-        upd_tab[buf][c0 + j] = make_float2(alpha, beta * kh);
-      }
-    }
+  for (int t = j.t0; t < j.t1; ++t, buf ^= 1) {
+    const float v_mine = holds_a ? load_scalar<QBF16>(a.v, (static_cast<int64_t>(t) * a.HV + j.hv) * DV + my_col) : 0.0f;
+    const TokenScalars ts = token_setup<DK, CPL, QBF16>(a, j, t, c0, chan_lane, dtb, amp, red_tab[buf], upd_tab[buf]);
     __syncthreads();
 
     // ---- one sweep: a = (kh*alpha)^T S, b = (qh*alpha)^T S, partial over rows ----
     float acc[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+    for (int m = 0; m < 8; ++m) acc[m] = 0.0f;
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       const float2 p = red_tab[buf][rs + RS * i];
@@ -329,8 +420,7 @@ __global__ __launch_bounds__(kWave) void kda_decode_kernel(const DecodeArgs a) {
       float v2[2];
 #pragma unroll
       for (int m = 0; m < 2; ++m) v2[m] = swap16_add(v4[m], v4[m + 2]);
-      const bool up = (rs & 1) != 0;
-      red = (up ? v2[1] : v2[0]) + dpp<kDppRowRor8>(up ? v2[0] : v2[1]);
+      red = dpp_level<8>((rs & 1) != 0, v2[0], v2[1]);
     } else {
       float v4[4];
       {
@@ -364,67 +454,221 @@ __global__ __launch_bounds__(kWave) void kda_decode_kernel(const DecodeArgs a) {
     const float4 u4 = *reinterpret_cast<const float4*>(&u_tab[4 * cq]);
     if (!holds_a && rs < 8) {
       const float uj = (rs & 2) ? ((rs & 1) ? u4.w : u4.z) : ((rs & 1) ? u4.y : u4.x);
-      store_scalar<BF16>(a.out, (static_cast<int64_t>(t) * a.HV + hv) * DV + my_col,
-                         fmaf(beta * qk, uj, red));
+      store_scalar<QBF16>(a.out, (static_cast<int64_t>(t) * a.HV + j.hv) * DV + my_col,
+                          fmaf(ts.beta * ts.qk, uj, red));
     }
-    const float u[4] = {u4.x, u4.y, u4.z, u4.w};
 
     // ---- S = alpha*S + (beta*kh) u^T ----
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       const float2 p = upd_tab[buf][rs + RS * i];
-      S[i].x = fmaf(p.y, u[0], p.x * S[i].x);
-      S[i].y = fmaf(p.y, u[1], p.x * S[i].y);
-      S[i].z = fmaf(p.y, u[2], p.x * S[i].z);
-      S[i].w = fmaf(p.y, u[3], p.x * S[i].w);
+      S[i].x = fmaf(p.y, u4.x, p.x * S[i].x);
+      S[i].y = fmaf(p.y, u4.y, p.x * S[i].y);
+      S[i].z = fmaf(p.y, u4.z, p.x * S[i].z);
+      S[i].w = fmaf(p.y, u4.w, p.x * S[i].w);
     }
   }
 
   // state tile: one trip out, to the same slot
 #pragma unroll
-  for (int i = 0; i < R; ++i) store_state(S_res, S_voff, i * kRowStep, S[i]);
+  for (int i = 0; i < R; ++i) IO::store(res, voff, i * kRowStep, S[i]);
 }
 
-template <int DK, int DV, bool BF16, int GATE>
+// ---------------------------------------------------------------------------
+// value-first layout: state [dv][dk]
+// ---------------------------------------------------------------------------
+
+template <int N>
+constexpr int log2_exact() {
+  static_assert(N > 0 && (N & (N - 1)) == 0, "power of two");
+  int l = 0;
+  while ((1 << l) < N) ++l;
+  return l;
+}
+
+template <int DK, int DV, bool QBF16, bool SBF16>
+__global__ __launch_bounds__(kWave) void kda_decode_vfirst(const DecodeArgs a) {
+  constexpr int CW = DV < 32 ? DV : 32;   // value rows of the wave's slab
+  constexpr int SLABS = DV / CW;
+  constexpr int KC = DK / 4;              // lanes across one row (4 keys each)
+  constexpr int RPI = kWave / KC;         // rows per load instruction
+  constexpr int L = CW / RPI;             // rows per lane
+  constexpr int NV = 2 * L;               // partial sums per lane (a and b)
+  constexpr int LOG_KC = log2_exact<KC>();
+  constexpr int LOG_NV = log2_exact<NV>();
+  constexpr int CPL = DK >= 2 * kWave ? DK / kWave : 1;
+  static_assert(L >= 1 && LOG_NV <= LOG_KC, "tile shape");
+  static_assert(CPL * kWave >= DK && CPL <= 2, "setup split");
+  using IO = StateIO<SBF16>;
+
+  __shared__ __attribute__((aligned(16))) float2 red_tab[2][DK];
+  __shared__ __attribute__((aligned(16))) float2 upd_tab[2][DK];
+  __shared__ __attribute__((aligned(16))) float u_tab[CW];   // [RPI][L]
+
+  const int lane = threadIdx.x;
+  const int kc = lane % KC;
+  const int rsub = lane / KC;
+  const TileJob j = resolve_job<SLABS>(a);
+  if (j.slot < 0 || j.slot >= a.N) {
+    zero_rows<DV, CW, QBF16>(a, j, lane);
+    return;
+  }
+  if (j.t0 == j.t1) return;
+
+  const int c0 = lane * CPL;
+  const bool chan_lane = c0 < DK;
+  float dtb[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) dtb[c] = 0.0f;
+  if (chan_lane) load_f32<CPL>(a.dt_bias + static_cast<int64_t>(j.hv) * DK + c0, dtb);
+  const float amp = exp_f(a.a_log[j.hv]);
+
+  // state tile: one trip in; lane rows are row0 + RPI*i
+  const int row0 = j.slab * CW + rsub;
+  char* const tile = static_cast<char*>(a.state_pool) +
+                     (static_cast<int64_t>(j.slot) * a.HV + j.hv) * (DK * DV * IO::kElem);
+  const __amdgpu_buffer_rsrc_t res = tile_resource(tile, DK * DV * IO::kElem);
+  const int voff = (row0 * DK + 4 * kc) * IO::kElem;
+  constexpr int kRowStep = RPI * DK * IO::kElem;
+  float4 S[L];
+#pragma unroll
+  for (int i = 0; i < L; ++i) S[i] = IO::load(res, voff, i * kRowStep);
+
+  // After the reduction lane kc holds value m (see below): an a-value of
+  // row i when m < L, else the b-value of row i = m - L.
+  const int m_final = (kc >> (LOG_KC - LOG_NV)) & (NV - 1);
+  const bool holds_a = m_final < L;
+  const int i_final = m_final & (L - 1);
+  const bool owner = (kc & ((1 << (LOG_KC - LOG_NV)) - 1)) == 0;   // not a duplicate
+  const int my_row = row0 + RPI * i_final;
+
+  int buf = 0;
+  for (int t = j.t0; t < j.t1; ++t, buf ^= 1) {
+    const float v_mine = holds_a ? load_scalar<QBF16>(a.v, (static_cast<int64_t>(t) * a.HV + j.hv) * DV + my_row) : 0.0f;
+    const TokenScalars ts = token_setup<DK, CPL, QBF16>(a, j, t, c0, chan_lane, dtb, amp, red_tab[buf], upd_tab[buf]);
+    __syncthreads();
+
+    // ---- sweep: per row, a and b partial over this lane's 4 keys ----
+    const float4 r01 = *reinterpret_cast<const float4*>(&red_tab[buf][4 * kc]);
+    const float4 r23 = *reinterpret_cast<const float4*>(&red_tab[buf][4 * kc + 2]);
+    float vals[NV];
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      vals[i] = fmaf(r01.x, S[i].x, fmaf(r01.z, S[i].y, fmaf(r23.x, S[i].z, r23.z * S[i].w)));
+      vals[L + i] = fmaf(r01.y, S[i].x, fmaf(r01.w, S[i].y, fmaf(r23.y, S[i].z, r23.w * S[i].w)));
+    }
+
+    // ---- transpose-reduce over the KC lanes of a row ----
+    // Level s uses lane bit LOG_KC-1-s and halves the values a lane carries;
+    // lanes with the bit clear keep the lower half.  After LOG_NV levels a
+    // lane holds value m_final; remaining lane bits only add duplicates.
+    if constexpr (KC == 32 && NV == 32) {
+      // lane bits 4..0: one row swap, then DPP moves inside the row
+#pragma unroll
+      for (int m = 0; m < 16; ++m) vals[m] = swap16_add(vals[m], vals[m + 16]);
+      const bool b3 = (kc & 8) != 0, b2 = (kc & 4) != 0, b1 = (kc & 2) != 0, b0 = (kc & 1) != 0;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) vals[m] = dpp_level<8>(b3, vals[m], vals[m + 8]);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) vals[m] = dpp_level<4>(b2, vals[m], vals[m + 4]);
+#pragma unroll
+      for (int m = 0; m < 2; ++m) vals[m] = dpp_level<2>(b1, vals[m], vals[m + 2]);
+      vals[0] = dpp_level<1>(b0, vals[0], vals[1]);
+    } else {
+#pragma unroll
+      for (int s = 0; s < LOG_NV; ++s) {
+        const int bit = LOG_KC - 1 - s;
+        const int half = NV >> (s + 1);
+        const bool up = ((kc >> bit) & 1) != 0;
+#pragma unroll
+        for (int m = 0; m < half; ++m) {
+          const float send = up ? vals[m] : vals[m + half];
+          const float keep = up ? vals[m + half] : vals[m];
+          vals[m] = keep + __shfl_xor(send, 1 << bit, kWave);
+        }
+      }
+#pragma unroll
+      for (int bit = LOG_KC - LOG_NV - 1; bit >= 0; --bit) vals[0] += __shfl_xor(vals[0], 1 << bit, kWave);
+    }
+    const float red = vals[0];
+
+    // ---- u = v - a (to every lane of the row); o = b + beta*(qh.kh)*u ----
+    if (holds_a && owner) u_tab[rsub * L + i_final] = v_mine - red;
+    __syncthreads();
+    if (!holds_a && owner)
+      store_scalar<QBF16>(a.out, (static_cast<int64_t>(t) * a.HV + j.hv) * DV + my_row,
+                          fmaf(ts.beta * ts.qk, u_tab[rsub * L + i_final], red));
+
+    // ---- S = alpha*S + (beta*kh) u^T ----
+    const float4 p01 = *reinterpret_cast<const float4*>(&upd_tab[buf][4 * kc]);
+    const float4 p23 = *reinterpret_cast<const float4*>(&upd_tab[buf][4 * kc + 2]);
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      const float u = u_tab[rsub * L + i];
+      S[i].x = fmaf(p01.y, u, p01.x * S[i].x);
+      S[i].y = fmaf(p01.w, u, p01.z * S[i].y);
+      S[i].z = fmaf(p23.y, u, p23.x * S[i].z);
+      S[i].w = fmaf(p23.w, u, p23.z * S[i].w);
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < L; ++i) IO::store(res, voff, i * kRowStep, S[i]);
+}
+
+// ---------------------------------------------------------------------------
+// dispatch
+// ---------------------------------------------------------------------------
+
+template <int DK, int DV, bool QBF16, bool SBF16, int LAYOUT>
 hipError_t launch_one(const DecodeArgs& args, hipStream_t stream) {
   constexpr int CW = DV < 32 ? DV : 32;
   const int64_t nwg = static_cast<int64_t>(args.B) * args.HV * (DV / CW);
   void* kargs[] = {const_cast<DecodeArgs*>(&args)};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&kda_decode_kernel<DK, DV, BF16, GATE>),
-                         dim3(static_cast<uint32_t>(nwg)), dim3(kWave), kargs, 0, stream);
+  const void* fn = LAYOUT == KDA_STATE_K_FIRST
+                       ? reinterpret_cast<const void*>(&kda_decode_kfirst<DK, DV, QBF16, SBF16>)
+                       : reinterpret_cast<const void*>(&kda_decode_vfirst<DK, DV, QBF16, SBF16>);
+  return hipLaunchKernel(fn, dim3(static_cast<uint32_t>(nwg)), dim3(kWave), kargs, 0, stream);
 }
 
 using LaunchFn = hipError_t (*)(const DecodeArgs&, hipStream_t);
 
 template <int DK, int DV>
-constexpr LaunchFn pick(bool bf16, int gate) {
-  return bf16 ? (gate == KDA_GATE_SOFTPLUS ? &launch_one<DK, DV, true, KDA_GATE_SOFTPLUS>
-                                           : &launch_one<DK, DV, true, KDA_GATE_LOWER_BOUND>)
-              : (gate == KDA_GATE_SOFTPLUS ? &launch_one<DK, DV, false, KDA_GATE_SOFTPLUS>
-                                           : &launch_one<DK, DV, false, KDA_GATE_LOWER_BOUND>);
+LaunchFn pick(bool qbf16, bool sbf16, int layout) {
+  const int key = (qbf16 ? 4 : 0) + (sbf16 ? 2 : 0) + (layout == KDA_STATE_V_FIRST ? 1 : 0);
+  switch (key) {
+    case 0: return &launch_one<DK, DV, false, false, KDA_STATE_K_FIRST>;
+    case 1: return &launch_one<DK, DV, false, false, KDA_STATE_V_FIRST>;
+    case 2: return &launch_one<DK, DV, false, true, KDA_STATE_K_FIRST>;
+    case 3: return &launch_one<DK, DV, false, true, KDA_STATE_V_FIRST>;
+    case 4: return &launch_one<DK, DV, true, false, KDA_STATE_K_FIRST>;
+    case 5: return &launch_one<DK, DV, true, false, KDA_STATE_V_FIRST>;
+    case 6: return &launch_one<DK, DV, true, true, KDA_STATE_K_FIRST>;
+    default: return &launch_one<DK, DV, true, true, KDA_STATE_V_FIRST>;
+  }
 }
 
 template <int DK>
-LaunchFn pick_dv(int dv, bool bf16, int gate) {
+LaunchFn pick_dv(int dv, bool qbf16, bool sbf16, int layout) {
   switch (dv) {
-    case 16: return pick<DK, 16>(bf16, gate);
-    case 32: return pick<DK, 32>(bf16, gate);
-    case 64: return pick<DK, 64>(bf16, gate);
-    case 128: return pick<DK, 128>(bf16, gate);
+    case 16: return pick<DK, 16>(qbf16, sbf16, layout);
+    case 32: return pick<DK, 32>(qbf16, sbf16, layout);
+    case 64: return pick<DK, 64>(qbf16, sbf16, layout);
+    case 128: return pick<DK, 128>(qbf16, sbf16, layout);
     default: return nullptr;
   }
 }
 
 }  // namespace
 
-int launch_decode(const DecodeArgs& args, int dk, int dv, bool bf16, int gate_mode,
-                  hipStream_t stream) {
+int launch_decode(const DecodeArgs& args, int dk, int dv, bool qkv_bf16, bool state_bf16,
+                  int state_layout, hipStream_t stream) {
   LaunchFn fn = nullptr;
   switch (dk) {
-    case 16: fn = pick_dv<16>(dv, bf16, gate_mode); break;
-    case 32: fn = pick_dv<32>(dv, bf16, gate_mode); break;
-    case 64: fn = pick_dv<64>(dv, bf16, gate_mode); break;
-    case 128: fn = pick_dv<128>(dv, bf16, gate_mode); break;
+    case 16: fn = pick_dv<16>(dv, qkv_bf16, state_bf16, state_layout); break;
+    case 32: fn = pick_dv<32>(dv, qkv_bf16, state_bf16, state_layout); break;
+    case 64: fn = pick_dv<64>(dv, qkv_bf16, state_bf16, state_layout); break;
+    case 128: fn = pick_dv<128>(dv, qkv_bf16, state_bf16, state_layout); break;
     default: break;
   }
   if (fn == nullptr) return KDA_ERR_UNSUPPORTED;

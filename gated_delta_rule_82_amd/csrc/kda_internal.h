@@ -19,17 +19,18 @@ struct DecodeArgs {
   const float* a_log;           // [HV]
   const float* dt_bias;         // [HV, dk]
   const int32_t* cu_seqlens;    // [B + 1]
-  float* state_pool;            // [N, HV, dk, dv]
+  void* state_pool;             // [N, HV, dk, dv] or [N, HV, dv, dk], f32 or bf16
   const int32_t* state_indices; // [B]
   int32_t B, T, H, HV, G, N;
+  int32_t gate_mode;            // enum kda_gate_mode
   float lower_bound, l2_eps, scale;
 };
 
-// Enqueue the decode kernel for (dk, dv, qkv dtype, gate mode) on `stream`.
-// Returns KDA_OK, KDA_ERR_UNSUPPORTED (no such specialization) or
-// KDA_ERR_LAUNCH.  Defined in kda_decode.hip.
-int launch_decode(const DecodeArgs& args, int dk, int dv, bool bf16, int gate_mode,
-                  hipStream_t stream);
+// Enqueue the decode kernel for (dk, dv, q/k/v dtype, state dtype, state
+// layout) on `stream`.  Returns KDA_OK, KDA_ERR_UNSUPPORTED (no such
+// specialization) or KDA_ERR_LAUNCH.  Defined in kda_decode.hip.
+int launch_decode(const DecodeArgs& args, int dk, int dv, bool qkv_bf16, bool state_bf16,
+                  int state_layout, hipStream_t stream);
 
 }  // namespace kda
 

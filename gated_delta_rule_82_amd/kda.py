@@ -32,6 +32,10 @@ KDA_GATE_SOFTPLUS = 0
 KDA_GATE_LOWER_BOUND = 1
 GATE_MODES = {"softplus": KDA_GATE_SOFTPLUS, "lower_bound": KDA_GATE_LOWER_BOUND}
 
+KDA_STATE_K_FIRST = 0
+KDA_STATE_V_FIRST = 1
+STATE_LAYOUTS = {"k_first": KDA_STATE_K_FIRST, "v_first": KDA_STATE_V_FIRST}
+
 EXPORTED_SYMBOLS = ("kda_decode", "kda_check_host", "kda_status_string", "kda_abi_version")
 
 
@@ -42,7 +46,8 @@ class KdaTensor(ctypes.Structure):
 
 class KdaMode(ctypes.Structure):
     _fields_ = [("gate_mode", ctypes.c_int32), ("lower_bound", ctypes.c_float),
-                ("l2_eps", ctypes.c_float), ("scale", ctypes.c_float)]
+                ("l2_eps", ctypes.c_float), ("scale", ctypes.c_float),
+                ("state_layout", ctypes.c_int32)]
 
 
 class KdaError(RuntimeError):
@@ -93,9 +98,11 @@ def status_string(code: int) -> str:
         return "libkda not built"
 
 
-def make_mode(gate_mode="softplus", lower_bound=0.0, l2_eps=0.0, scale=0.0) -> KdaMode:
+def make_mode(gate_mode="softplus", lower_bound=0.0, l2_eps=0.0, scale=0.0,
+              state_layout="k_first") -> KdaMode:
     gm = GATE_MODES[gate_mode] if isinstance(gate_mode, str) else int(gate_mode)
-    return KdaMode(gm, float(lower_bound), float(l2_eps), float(scale))
+    sl = STATE_LAYOUTS[state_layout] if isinstance(state_layout, str) else int(state_layout)
+    return KdaMode(gm, float(lower_bound), float(l2_eps), float(scale), sl)
 
 
 def raw_tensor(data_ptr: int, dtype: int, shape) -> KdaTensor:
@@ -139,12 +146,14 @@ ARG_NAMES = ("out", "q", "k", "v", "raw_gate", "beta_logits", "a_log", "dt_bias"
 
 def decode(out, q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens, state_pool,
            state_indices, *, gate_mode="softplus", lower_bound=0.0, l2_eps=0.0, scale=0.0,
-           stream: Optional[int] = None) -> None:
+           state_layout="k_first", stream: Optional[int] = None) -> None:
     """Advance the KDA decode recurrence in place (see include/kda.h).
 
     Tensors are torch GPU tensors with the shapes of kda.h; ``out`` and
-    ``state_pool`` are written.  The work is enqueued on ``stream`` (a raw
-    hipStream_t handle; default: torch's current stream of q's device)."""
+    ``state_pool`` are written.  ``state_pool`` is float32 or bfloat16, laid
+    out [N, HV, dk, dv] ("k_first") or [N, HV, dv, dk] ("v_first").  The work
+    is enqueued on ``stream`` (a raw hipStream_t handle; default: torch's
+    current stream of q's device)."""
     import torch
     tensors = (out, q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens, state_pool,
                state_indices)
@@ -153,7 +162,7 @@ def decode(out, q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens, stat
     for t, n in zip(tensors, ARG_NAMES):
         if t.device != dev:
             raise ValueError(f"{n}: on {t.device}, expected {dev}")
-    mode = make_mode(gate_mode, lower_bound, l2_eps, scale)
+    mode = make_mode(gate_mode, lower_bound, l2_eps, scale, state_layout)
     with torch.cuda.device(dev):
         if stream is None:
             stream = torch.cuda.current_stream(dev).cuda_stream

@@ -45,11 +45,23 @@ class Workload:
     cu_seqlens: Optional[Tuple[int, ...]] = None
     state_indices: Optional[Tuple[int, ...]] = None
     host_state: bool = False          # draw touched tiles on the host
+    state_layout: str = "k_first"     # "k_first" [N,HV,DK,DV] or "v_first" [N,HV,DV,DK]
+    state_dtype: str = "f32"          # "f32" or "bf16"
     description: str = field(default="", compare=False)
 
     @property
     def G(self) -> int:
         return self.HV // self.H
+
+    @property
+    def pool_shape(self):
+        if self.state_layout == "v_first":
+            return (self.n_slots, self.HV, self.DV, self.DK)
+        return (self.n_slots, self.HV, self.DK, self.DV)
+
+    @property
+    def state_elem_bytes(self) -> int:
+        return 2 if self.state_dtype == "bf16" else 4
 
 
 PRESETS = {
@@ -164,8 +176,10 @@ def draw(cfg: Workload) -> Inputs:
 
 
 def host_pool(inp: Inputs, fill_sigma: Optional[float] = None, seed_offset: int = 1) -> np.ndarray:
-    """Full fp32 pool on the host: the touched tiles from ``inp`` and every
-    other slot drawn from its own generator (seed + seed_offset)."""
+    """Full pool on the host as fp32 values, in the workload's layout: the
+    touched tiles from ``inp`` and every other slot drawn from its own
+    generator (seed + seed_offset).  For a bf16 pool the values are rounded
+    to bf16 (nearest-even), i.e. they are exactly what the device holds."""
     cfg = inp.cfg
     rng = np.random.default_rng(cfg.seed + seed_offset)
     sigma = cfg.state_sigma if fill_sigma is None else fill_sigma
@@ -175,6 +189,10 @@ def host_pool(inp: Inputs, fill_sigma: Optional[float] = None, seed_offset: int 
         for b, slot in enumerate(inp.state_indices):
             if slot >= 0:
                 pool[slot] = inp.touched_state[b]
+    if cfg.state_layout == "v_first":
+        pool = np.ascontiguousarray(np.swapaxes(pool, 2, 3))
+    if cfg.state_dtype == "bf16":
+        pool = bf16_bits_to_f32(f32_to_bf16_bits(pool))
     return pool
 
 
@@ -217,11 +235,12 @@ def device_pool(inp: Inputs, device="cuda", seed_offset: int = 1):
     generator (N(0, sigma)), which keeps multi-GB pools off the host."""
     import torch
     cfg = inp.cfg
+    dt = torch.bfloat16 if cfg.state_dtype == "bf16" else torch.float32
     if cfg.host_state:
-        return torch.from_numpy(host_pool(inp, seed_offset=seed_offset)).to(device)
+        return torch.from_numpy(host_pool(inp, seed_offset=seed_offset)).to(device).to(dt)
     gen = torch.Generator(device=device)
     gen.manual_seed(cfg.seed + seed_offset)
-    pool = torch.empty((cfg.n_slots, cfg.HV, cfg.DK, cfg.DV), dtype=torch.float32, device=device)
+    pool = torch.empty(cfg.pool_shape, dtype=dt, device=device)
     pool.normal_(0.0, cfg.state_sigma, generator=gen)
     return pool
 
@@ -231,7 +250,7 @@ def state_bytes(cfg: Workload, inp: Inputs) -> int:
     with at least one token and a valid slot is read once and written once."""
     counts = np.diff(inp.cu_seqlens)
     active = int(np.sum((counts > 0) & (inp.state_indices >= 0)))
-    return active * cfg.HV * 2 * cfg.DK * cfg.DV * 4
+    return active * cfg.HV * 2 * cfg.DK * cfg.DV * cfg.state_elem_bytes
 
 
 def token_bytes(cfg: Workload, inp: Inputs) -> int:

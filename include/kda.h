@@ -6,20 +6,26 @@
  * operation and the tensor contract follow:
  *   - "KdaDecode" (Modular MAX Mojo builtin kernels), Tensor Shapes and
  *     default parameters: packed [1, total_T, ...] token tensors, a slotted
- *     key-first state pool [max_slots, HV, dk, dv] mutated in place through
- *     state_indices, cu_seqlens varlen packing, the "original" stable-softplus
- *     gate and beta given as logits;
+ *     state pool [max_slots, HV, dk, dv] (key-first; the state_layout
+ *     parameter also names the value-first transpose, and state_dtype a
+ *     non-fp32 pool) mutated in place through state_indices, cu_seqlens
+ *     varlen packing, the "original" stable-softplus gate and beta given as
+ *     logits;
  *   - "Delta-rule write" (atlas, Kimi-K3 > Kimi Delta Attention), code
  *     excerpt naive_recurrent_kda: per token, decay the state row k by
  *     exp(g[k]), write (beta*k) outer (v - k^T S), read o = q^T S from the
  *     updated state; q and k repeated over G = HV/H value heads; the output
  *     takes v's dtype;
+ *   - the same "Delta-rule write" page, modeling_kimi_linear.py excerpt: the
+ *     model calls the recurrent kernel with transpose_state_layout=True,
+ *     i.e. a value-first state;
  *   - "KDA Block TKG Kernel API Reference" (AWS Neuron NKI): l2_eps = 1e-6,
  *     the query scale folded into the L2-normalised query, and the
  *     lower-bound gate (parameters A_log, dt_bias, lower_bound).
  *
  * Per token t of request b, for value head hv with key head h = hv / G and
- * state S = state_pool[state_indices[b], hv] (fp32, S[k][v]):
+ * state S = state_pool[state_indices[b], hv] (S[k][v]; the value-first
+ * layout stores its transpose):
  *     qh = scale * q[t,h] / sqrt(sum q[t,h]^2 + l2_eps)
  *     kh =         k[t,h] / sqrt(sum k[t,h]^2 + l2_eps)
  *     x  = raw_gate[t,hv] + dt_bias[hv]                       (per channel)
@@ -48,7 +54,7 @@ extern "C" {
 /* hipStream_t, declared here so that this header needs no HIP include. */
 typedef struct ihipStream_t* hipStream_t;
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 /* Status codes.  Zero is success; errors are negative. */
 enum kda_status {
@@ -58,7 +64,8 @@ enum kda_status {
   KDA_ERR_SHAPE = -3,       /* ranks or extents disagree (incl. HV % H)     */
   KDA_ERR_UNSUPPORTED = -4, /* dk or dv outside {16, 32, 64, 128}, or a    */
                             /* mix of dtypes that has no kernel             */
-  KDA_ERR_MODE = -5,        /* bad gate mode, lower_bound, l2_eps or scale  */
+  KDA_ERR_MODE = -5,        /* bad gate mode, lower_bound, l2_eps, scale or */
+                            /* state layout                                 */
   KDA_ERR_LAUNCH = -6,      /* the HIP launch itself reported an error      */
   KDA_ERR_PRECONDITION = -7 /* kda_check_host: cu_seqlens / indices invalid */
 };
@@ -76,6 +83,12 @@ enum kda_gate_mode {
   KDA_GATE_LOWER_BOUND = 1  /* g = lower_bound * sigmoid(exp(A_log) * x)  */
 };
 
+/* Layout of one (slot, value head) state tile, "KdaDecode" state_layout. */
+enum kda_state_layout {
+  KDA_STATE_K_FIRST = 0,    /* [dk][dv]: S[k][v] (the default)             */
+  KDA_STATE_V_FIRST = 1     /* [dv][dk]: the transposed layout             */
+};
+
 /* A dense row-major tensor: `data` points at element [0,...,0]; the extents
  * are shape[0..ndim-1] and the storage is contiguous (no strides). */
 typedef struct kda_tensor {
@@ -91,6 +104,7 @@ typedef struct kda_mode {
   float lower_bound;   /* lower-bound mode only: finite and <= 0              */
   float l2_eps;        /* >= 0, finite; 0 selects the default 1e-6            */
   float scale;         /* > 0, finite; 0 selects the default dk^-0.5          */
+  int32_t state_layout;/* enum kda_state_layout                               */
 } kda_mode;
 
 /*
@@ -107,7 +121,11 @@ typedef struct kda_mode {
  *   a_log         [HV]            f32.
  *   dt_bias       [HV, dk]        f32.
  *   cu_seqlens    [B + 1]         i32, device resident.
- *   state_pool    [N, HV, dk, dv] f32, key-first, updated in place.
+ *   state_pool    [N, HV, dk, dv] (KDA_STATE_K_FIRST) or [N, HV, dv, dk]
+ *                 (KDA_STATE_V_FIRST), f32 or bf16, updated in place.  A
+ *                 bf16 pool is widened to fp32 on load, advanced in fp32
+ *                 through all of the request's tokens and rounded to
+ *                 nearest-even once when written back.
  *   state_indices [B]             i32, device resident.
  *   mode          scalar parameters (see kda_mode).
  *   stream        HIP stream to enqueue on (NULL = the null stream).

@@ -7,6 +7,8 @@ from .kda_oracle import (  # noqa: F401
     DEFAULT_L2_EPS,
     GATE_LOWER_BOUND,
     GATE_SOFTPLUS,
+    STATE_K_FIRST,
+    STATE_V_FIRST,
     decay,
     decode_tile,
     delta_write,

@@ -28,7 +28,12 @@ the design notes of the repository):
   * the query scale multiplies the normalised query once; default dk**-0.5.
   * a negative state index means "skip": no state access, output rows zero.
   * an empty request (no tokens) leaves its state untouched.
-  * state layout is key-first: S[k, v].
+  * state layout: key-first S[k, v] ([KDD] default state_layout); the
+    value-first pool stores each tile transposed, S[v, k] (the layout [FWD]
+    asks for with transpose_state_layout=True).  The recurrence is the same.
+  * state dtype ([KDD] names state_dtype without its arithmetic): a bf16
+    pool is read exactly, advanced in high precision through all of the
+    request's tokens, and rounded to nearest-even when stored.
 
 Parity status: every function below is pinned by the CPU tests
 (``tests/test_oracle_pins.py``) against closed forms, hand-worked values,
@@ -43,6 +48,8 @@ import numpy as np
 GATE_SOFTPLUS = "softplus"
 GATE_LOWER_BOUND = "lower_bound"
 DEFAULT_L2_EPS = 1e-6
+STATE_K_FIRST = "k_first"
+STATE_V_FIRST = "v_first"
 
 
 # ----------------------------------------------------------------------------
@@ -176,7 +183,7 @@ def _drop_batch_axis(x, name):
 def kda_decode(q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens,
                state_pool, state_indices, *, gate_mode=GATE_SOFTPLUS,
                lower_bound=None, l2_eps=DEFAULT_L2_EPS, scale=None,
-               tiles=None):
+               tiles=None, state_layout=STATE_K_FIRST, state_dtype="f32"):
     """The decode op over a cu_seqlens-packed batch and a slotted state pool.
 
     Shapes follow [KDD] Tensor Shapes: q, k [1, T, H, dk]; v [1, T, HV, dv];
@@ -190,9 +197,12 @@ def kda_decode(q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens,
     repeated G times along the head axis).
 
     ``state_pool`` may be an array (returned updated as an fp64 copy) or a
-    dict {(slot, hv): [dk, dv] array} holding only the tiles needed; in that
-    case ``tiles`` lists the (b, hv) pairs to compute and the dict returned
-    holds their advanced states.  Output rows not computed are NaN.
+    dict {(slot, hv): tile} holding only the tiles needed; in that case
+    ``tiles`` lists the (b, hv) pairs to compute and the dict returned holds
+    their advanced states.  Output rows not computed are NaN.  With
+    ``state_layout="v_first"`` every tile is stored transposed ([dv, dk]);
+    with ``state_dtype="bf16"`` each advanced tile is rounded to bfloat16
+    (nearest-even) when stored.
 
     Returns (out [1, T, HV, dv] fp64, advanced pool).
     """
@@ -234,10 +244,20 @@ def kda_decode(q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens,
             continue
         h = hv // G
         S0 = pool[(slot, hv)] if as_dict else pool[slot, hv]
+        if state_layout == STATE_V_FIRST:
+            S0 = S0.T
+        elif state_layout != STATE_K_FIRST:
+            raise ValueError(f"unknown state layout {state_layout!r}")
         o, S = decode_tile(S0, q[t0:t1, h], k[t0:t1, h], v[t0:t1, hv],
                            raw_gate[t0:t1, hv], beta_logits[t0:t1, hv],
                            a_log[hv], dt_bias[hv], gate_mode=gate_mode,
                            lower_bound=lower_bound, l2_eps=l2_eps, scale=scale)
+        if state_dtype == "bf16":
+            S = round_to_bf16(S)
+        elif state_dtype != "f32":
+            raise ValueError(f"unknown state dtype {state_dtype!r}")
+        if state_layout == STATE_V_FIRST:
+            S = S.T
         out[t0:t1, hv] = o
         if as_dict:
             pool[(slot, hv)] = S

@@ -8,6 +8,8 @@ Tolerances (fixed here, used by every GPU parity test):
     |o_gpu - o_ref| <= 1 bf16 ulp of o_ref + 1e-5 * max|o_ref| (the rounding
     to bf16 costs half an ulp; fp32 arithmetic adds far less than the rest).
   * fp32 output: max|do| / max|o_ref| <= 1e-5.
+  * bf16 state pool: both sides round the advanced state to bf16 once, so
+    per element |S_gpu - S_ref| <= 1 bf16 ulp of S_ref (+ 1e-6 * max|S_ref|).
   * state_indices gathers: every slot not named in state_indices is
     bit-identical after the call.
 """
@@ -23,6 +25,7 @@ STATE_TIGHT = 2e-6
 OUT_ABS_REQUIRED = 2e-2
 OUT_ULP_FLOOR = 1e-5
 OUT_F32_REL = 1e-5
+STATE_BF16_FLOOR = 1e-6
 
 
 def bf16_ulp(x):
@@ -40,7 +43,7 @@ def gather_tiles(pool_t, slots, hvs):
     import torch
     s = torch.as_tensor(np.asarray(slots, dtype=np.int64), device=pool_t.device)
     h = torch.as_tensor(np.asarray(hvs, dtype=np.int64), device=pool_t.device)
-    return pool_t[s, h].cpu().numpy()
+    return pool_t[s, h].float().cpu().numpy()
 
 
 def choose_tiles(inp, sample, seed=123):
@@ -60,7 +63,7 @@ def run_gpu(inp, dev, pool_t, out_t=None, mode_overrides=None, stream=None):
     cfg = inp.cfg
     if out_t is None:
         out_t = wl.empty_out(inp, pool_t.device)
-    mode = dict(gate_mode=cfg.gate_mode, lower_bound=cfg.lower_bound)
+    mode = dict(gate_mode=cfg.gate_mode, lower_bound=cfg.lower_bound, state_layout=cfg.state_layout)
     if mode_overrides:
         mode.update(mode_overrides)
     kda.decode(out_t, dev["q"], dev["k"], dev["v"], dev["raw_gate"], dev["beta_logits"],
@@ -79,7 +82,8 @@ def oracle_tiles(inp, tiles, init_states, **mode):
     for (b, hv), S in zip(valid, init_states):
         pool[(int(inp.state_indices[b]), hv)] = S
     kw = dict(gate_mode=cfg.gate_mode,
-              lower_bound=cfg.lower_bound if cfg.gate_mode == ko.GATE_LOWER_BOUND else None)
+              lower_bound=cfg.lower_bound if cfg.gate_mode == ko.GATE_LOWER_BOUND else None,
+              state_layout=cfg.state_layout, state_dtype=cfg.state_dtype)
     kw.update(mode)
     return ko.kda_decode(inp.q, inp.k, inp.v, inp.raw_gate, inp.beta_logits, inp.a_log,
                          inp.dt_bias, inp.cu_seqlens, pool, inp.state_indices, tiles=tiles, **kw)
@@ -115,7 +119,16 @@ def compare_outputs(inp, tiles, out_gpu, out_ref):
     return stats
 
 
-def compare_states(states_gpu, states_ref):
+def compare_states(states_gpu, states_ref, state_dtype="f32"):
+    if state_dtype == "bf16":
+        # both sides round once to bf16: equal, or one ulp apart where the
+        # fp32 and fp64 results straddle a rounding boundary
+        worst = 0.0
+        for Sg, Sr in zip(states_gpu, states_ref):
+            bound = bf16_ulp(Sr) + STATE_BF16_FLOOR * float(np.max(np.abs(Sr)))
+            worst = max(worst, float(np.max(np.abs(Sg.astype(np.float64) - Sr) / bound)))
+        assert worst <= 1.0, f"bf16 state exceeds 1 ulp (ratio {worst:.3f})"
+        return {"state_ulp_ratio": worst}
     worst = 0.0
     for Sg, Sr in zip(states_gpu, states_ref):
         denom = float(np.max(np.abs(Sr)))
@@ -152,7 +165,7 @@ def parity_case(inp, device="cuda", sample=None, check_untouched=True, mode_over
     out_ref, pool_ref = oracle_tiles(inp, tiles, init, **(oracle_mode or {}))
     stats = compare_outputs(inp, tiles, out_gpu, out_ref)
     ref_states = [pool_ref[(s, hv)] for s, hv in zip(slots, hvs)]
-    stats.update(compare_states(after, ref_states) if valid else {})
+    stats.update(compare_states(after, ref_states, cfg.state_dtype) if valid else {})
     # skipped requests: zero rows
     for b, hv in tiles:
         if inp.state_indices[b] < 0:

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = kda.library()
-    assert lib.kda_abi_version() == 1
+    assert lib.kda_abi_version() == 2
     codes = [kda.KDA_OK, kda.KDA_ERR_NULL, kda.KDA_ERR_DTYPE, kda.KDA_ERR_SHAPE,
              kda.KDA_ERR_UNSUPPORTED, kda.KDA_ERR_MODE, kda.KDA_ERR_LAUNCH,
              kda.KDA_ERR_PRECONDITION]
@@ -135,7 +135,7 @@ def test_null_arguments():
 @pytest.mark.parametrize("name,dtype", [
     ("q", kda.KDA_F32), ("k", kda.KDA_F32), ("out", kda.KDA_F32), ("v", kda.KDA_I32),
     ("raw_gate", kda.KDA_BF16), ("beta_logits", kda.KDA_BF16), ("a_log", kda.KDA_I32),
-    ("dt_bias", kda.KDA_BF16), ("state_pool", kda.KDA_BF16), ("cu_seqlens", kda.KDA_F32),
+    ("dt_bias", kda.KDA_BF16), ("state_pool", kda.KDA_I32), ("cu_seqlens", kda.KDA_F32),
     ("state_indices", kda.KDA_F32),
 ])
 def test_dtype_errors(name, dtype):
@@ -194,3 +194,19 @@ def test_python_binding_rejects_cpu_tensors():
     t = torch.zeros(4)
     with pytest.raises(ValueError):
         kda.decode(*([t] * 11))
+
+
+def test_state_layout_and_dtype_checks():
+    # an invalid layout value is a mode error
+    assert call(descriptors(), state_layout=2) == kda.KDA_ERR_MODE
+    # value-first pools are [N, HV, dv, dk]: with dk != dv the key-first shape
+    # is rejected and the transposed one gets as far as the (invalid) gate mode
+    d = descriptors(DK=128, DV=64)
+    assert call(d, state_layout="v_first") == kda.KDA_ERR_SHAPE
+    d["state_pool"] = reshape(d["state_pool"], (8, 4, 64, 128))
+    assert call(d, state_layout="v_first", gate_mode=9) == kda.KDA_ERR_MODE
+    assert call(d, state_layout="k_first", gate_mode=9) == kda.KDA_ERR_SHAPE
+    # a bf16 pool passes the dtype check (stopped later by the invalid gate mode)
+    d = descriptors()
+    d["state_pool"] = kda.raw_tensor(d["state_pool"].data, kda.KDA_BF16, (8, 4, 128, 128))
+    assert call(d, gate_mode=9) == kda.KDA_ERR_MODE

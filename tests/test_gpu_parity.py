@@ -73,6 +73,31 @@ def test_head_dims_and_modes(torch_cuda, dk, dv, qkv, gate):
     H.parity_case(wl.draw(cfg))
 
 
+@pytest.mark.parametrize("dk,dv", list(itertools.product([16, 32, 64, 128], repeat=2)))
+@pytest.mark.parametrize("layout,sdt", [("v_first", "f32"), ("k_first", "bf16"), ("v_first", "bf16")])
+def test_state_layouts_and_dtypes(torch_cuda, dk, dv, layout, sdt):
+    gate = wl.LOWER_BOUND if (dk + dv) % 64 else wl.SOFTPLUS
+    qkv = "f32" if dk == dv == 16 else "bf16"
+    cfg = small(DK=dk, DV=dv, qkv=qkv, gate=gate, lb=-5.0 if gate == wl.LOWER_BOUND else 0.0,
+                seed=dk * 5 + dv, state_layout=layout, state_dtype=sdt)
+    _say("layout", layout, sdt, dk, dv, qkv, gate)
+    H.parity_case(wl.draw(cfg))
+
+
+@pytest.mark.parametrize("name,sample,layout,sdt", [
+    ("wide_b256_h96", 256, "v_first", "f32"),
+    ("wide_b256_h96", 256, "k_first", "bf16"),
+    ("varlen_gqa_b128", 512, "v_first", "f32"),
+    ("stress_b1024_n4", 128, "v_first", "bf16"),
+])
+def test_full_size_other_layouts(torch_cuda, name, sample, layout, sdt):
+    cfg = wl.preset(name, state_layout=layout, state_dtype=sdt)
+    _say(name, layout, sdt, "sampled tiles", sample)
+    stats, _, _ = H.parity_case(wl.draw(cfg), sample=sample)
+    print(name, layout, sdt, stats, flush=True)
+    torch_cuda.cuda.empty_cache()
+
+
 def test_ragged_grid_not_multiple_of_8(torch_cuda):
     cfg = small(B=37, H_=5, HV=5, tokens="u:0..3", slots=50, seed=5)
     _say("ragged", cfg)
@@ -97,11 +122,16 @@ def test_gqa_g4(torch_cuda):
 # special cases the method has
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("gate", [wl.SOFTPLUS, wl.LOWER_BOUND])
-def test_pass_through_is_bit_exact(torch_cuda, gate):
+@pytest.mark.parametrize("gate,layout,sdt", [(wl.SOFTPLUS, "k_first", "f32"),
+                                              (wl.LOWER_BOUND, "k_first", "f32"),
+                                              (wl.SOFTPLUS, "v_first", "f32"),
+                                              (wl.LOWER_BOUND, "v_first", "bf16"),
+                                              (wl.SOFTPLUS, "k_first", "bf16")])
+def test_pass_through_is_bit_exact(torch_cuda, gate, layout, sdt):
     """beta = 0 and g = 0 leave the state bit-identical."""
     torch = torch_cuda
-    cfg = small(B=4, tokens="u:1..3", gate=gate, lb=0.0, seed=21)
+    cfg = small(B=4, tokens="u:1..3", gate=gate, lb=0.0, seed=21, state_layout=layout,
+                state_dtype=sdt)
     inp = wl.draw(cfg)
     inp.beta_logits[:] = -np.inf
     if gate == wl.SOFTPLUS:
@@ -114,7 +144,7 @@ def test_pass_through_is_bit_exact(torch_cuda, gate):
     torch.cuda.synchronize()
     assert torch.equal(pool, before)
     tiles = H.choose_tiles(inp, None)
-    init = [before[int(inp.state_indices[b]), hv].cpu().numpy() for b, hv in tiles
+    init = [before[int(inp.state_indices[b]), hv].float().cpu().numpy() for b, hv in tiles
             if inp.state_indices[b] >= 0]
     ref, _ = H.oracle_tiles(inp, tiles, init)
     H.compare_outputs(inp, tiles, H.out_to_f64(out), ref)
@@ -131,9 +161,10 @@ def test_skip_index_and_empty_request(torch_cuda):
     assert np.isfinite(o).all()
 
 
-def test_deterministic_bitwise(torch_cuda):
+@pytest.mark.parametrize("layout", ["k_first", "v_first"])
+def test_deterministic_bitwise(torch_cuda, layout):
     torch = torch_cuda
-    cfg = small(B=16, HV=8, H_=4, tokens="u:1..6", seed=23)
+    cfg = small(B=16, HV=8, H_=4, tokens="u:1..6", seed=23, state_layout=layout)
     inp = wl.draw(cfg)
     _say("determinism", cfg)
     dev = wl.to_device(inp)
@@ -147,11 +178,12 @@ def test_deterministic_bitwise(torch_cuda):
                        o2.view(torch.int16) if o2.dtype == torch.bfloat16 else o2)
 
 
-def test_split_invariance(torch_cuda):
-    """One call over n tokens equals n calls of one token each."""
+@pytest.mark.parametrize("layout", ["k_first", "v_first"])
+def test_split_invariance(torch_cuda, layout):
+    """One call over n tokens equals n calls of one token each (fp32 state)."""
     torch = torch_cuda
     n = 5
-    cfg = small(B=3, tokens=str(n), seed=24)
+    cfg = small(B=3, tokens=str(n), seed=24, state_layout=layout)
     inp = wl.draw(cfg)
     _say("split", cfg)
     dev = wl.to_device(inp)
@@ -168,7 +200,8 @@ def test_split_invariance(torch_cuda):
         o = torch.empty((1, cfg.B, cfg.HV, cfg.DV), dtype=out_a.dtype, device=pool_b.device)
         from gated_delta_rule_82_amd import kda
         kda.decode(o, one["q"], one["k"], one["v"], one["raw_gate"], one["beta_logits"],
-                   one["a_log"], one["dt_bias"], one["cu_seqlens"], pool_b, one["state_indices"])
+                   one["a_log"], one["dt_bias"], one["cu_seqlens"], pool_b, one["state_indices"],
+                   state_layout=layout)
         outs.append(o)
     torch.cuda.synchronize()
     assert torch.allclose(pool_a, pool_b, rtol=0, atol=1e-6 * float(pool_a.abs().max()))

@@ -368,3 +368,46 @@ def test_tiny_workload_runs_and_is_finite():
                              inp.dt_bias, inp.cu_seqlens, pool, inp.state_indices)
     assert out.shape == (1, 5, 4, 16) and np.isfinite(out).all()
     assert np.array_equal(new[[1, 3]], pool[[1, 3]].astype(np.float64))
+
+
+# ---------------------------------------------------------------------------
+# state layout and state dtype
+# ---------------------------------------------------------------------------
+
+def test_value_first_pool_is_the_transposed_key_first_pool():
+    """A value-first pool holds each tile transposed; the recurrence and the
+    outputs are unchanged (dk != dv, so a wrong axis cannot pass)."""
+    d, cu, pool, idx = _small_batch(dk=8, dv=6)
+    out_k, new_k = ko.kda_decode(**d, cu_seqlens=cu, state_pool=pool, state_indices=idx)
+    pool_v = np.ascontiguousarray(np.swapaxes(pool, 2, 3))
+    out_v, new_v = ko.kda_decode(**d, cu_seqlens=cu, state_pool=pool_v, state_indices=idx,
+                                 state_layout=ko.STATE_V_FIRST)
+    # equal up to the summation order numpy's matmul picks for a transposed view
+    np.testing.assert_allclose(out_v, out_k, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(new_v, np.swapaxes(new_k, 2, 3), rtol=1e-13, atol=1e-15)
+    # a dict pool in the value-first layout takes [dv, dk] tiles
+    tiles = [(0, 1), (2, 3)]
+    sub = {(int(idx[b]), hv): pool_v[idx[b], hv] for b, hv in tiles}
+    out_s, new_s = ko.kda_decode(**d, cu_seqlens=cu, state_pool=sub, state_indices=idx,
+                                 tiles=tiles, state_layout=ko.STATE_V_FIRST)
+    for b, hv in tiles:
+        assert new_s[(int(idx[b]), hv)].shape == (6, 8)
+        np.testing.assert_allclose(new_s[(int(idx[b]), hv)], new_v[idx[b], hv], rtol=1e-13, atol=1e-15)
+
+
+def test_bf16_state_rounds_once_when_stored():
+    """A bf16 pool: outputs equal the fp64 run on the same (bf16-valued)
+    initial state, and the stored tile is the fp64 result rounded to
+    nearest-even, i.e. exactly representable in bf16."""
+    d, cu, pool, idx = _small_batch()
+    pool16 = ko.round_to_bf16(pool)
+    out_a, new_a = ko.kda_decode(**d, cu_seqlens=cu, state_pool=pool16, state_indices=idx)
+    out_b, new_b = ko.kda_decode(**d, cu_seqlens=cu, state_pool=pool16, state_indices=idx,
+                                 state_dtype="bf16")
+    assert np.array_equal(out_a, out_b)
+    touched = sorted(set(int(i) for i in idx))
+    assert np.array_equal(new_b[touched], ko.round_to_bf16(new_a[touched]))
+    bits = wl.f32_to_bf16_bits(new_b.astype(np.float32))
+    assert np.array_equal(wl.bf16_bits_to_f32(bits).astype(np.float64), new_b)
+    untouched = sorted(set(range(pool.shape[0])) - set(touched))
+    assert np.array_equal(new_b[untouched], pool16[untouched])
