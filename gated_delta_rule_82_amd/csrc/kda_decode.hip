@@ -63,11 +63,14 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
 }
 
 // fp32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN.
+// Both candidates are computed and one is selected: written as a branch,
+// the NaN test became divergent control flow around each conversion, and
+// ahead of a packed multi-value store that code produced wrong words.
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
-  uint32_t u = __float_as_uint(x);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t quiet_nan = (u >> 16) | 0x40u;
+  return (u & 0x7fffffffu) > 0x7f800000u ? quiet_nan : rounded;
 }
 
 // Transcendentals use the hardware exp2 / log2 / rcp / rsqrt instructions
@@ -165,29 +168,50 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_resource(void* tile, int 
   return __builtin_amdgcn_make_buffer_rsrc(tile, static_cast<short>(0), bytes, kRawBufferWord3);
 }
 
-// Four consecutive state elements of one row: fp32 (16 bytes) or bf16
-// (8 bytes, rounded to nearest-even on the way out).
-template <bool SBF16>
+// A lane moves its state in pieces of N consecutive values of one row: N = 4
+// fp32 (16 bytes) or N = 4 / 8 bf16 (8 / 16 bytes), widened to fp32 on the
+// way in and rounded to nearest-even on the way out.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+template <bool SBF16, int N>
 struct StateIO {
+  static_assert(N == 4 || (SBF16 && N == 8), "state access width");
   static constexpr int kElem = SBF16 ? 2 : 4;
-  __device__ static __forceinline__ float4 load(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-    if constexpr (SBF16) {
+  __device__ static __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int voff, int soff, float* x) {
+    if constexpr (SBF16 && N == 8) {
+      const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kCachePolicyNT);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[2 * e] = bf16_to_f32(w[e] & 0xffffu);
+        x[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+      }
+    } else if constexpr (SBF16) {
       const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kCachePolicyNT);
-      return make_float4(bf16_to_f32(w.x & 0xffffu), __uint_as_float(w.x & 0xffff0000u),
-                         bf16_to_f32(w.y & 0xffffu), __uint_as_float(w.y & 0xffff0000u));
+      x[0] = bf16_to_f32(w.x & 0xffffu);
+      x[1] = __uint_as_float(w.x & 0xffff0000u);
+      x[2] = bf16_to_f32(w.y & 0xffffu);
+      x[3] = __uint_as_float(w.y & 0xffff0000u);
     } else {
-      const f32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kCachePolicyNT);
-      return make_float4(x.x, x.y, x.z, x.w);
+      const f32x4 w = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kCachePolicyNT);
+      x[0] = w.x;
+      x[1] = w.y;
+      x[2] = w.z;
+      x[3] = w.w;
     }
   }
-  __device__ static __forceinline__ void store(__amdgpu_buffer_rsrc_t r, int voff, int soff, float4 v) {
-    if constexpr (SBF16) {
-      const u32x2 w = {f32_to_bf16_rne(v.x) | (f32_to_bf16_rne(v.y) << 16),
-                       f32_to_bf16_rne(v.z) | (f32_to_bf16_rne(v.w) << 16)};
+  __device__ static __forceinline__ void store(__amdgpu_buffer_rsrc_t r, int voff, int soff, const float* x) {
+    if constexpr (SBF16 && N == 8) {
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = f32_to_bf16_rne(x[2 * e]) | (f32_to_bf16_rne(x[2 * e + 1]) << 16);
+      __builtin_amdgcn_raw_buffer_store_b128(w, r, voff, soff, kCachePolicyNT);
+    } else if constexpr (SBF16) {
+      const u32x2 w = {f32_to_bf16_rne(x[0]) | (f32_to_bf16_rne(x[1]) << 16),
+                       f32_to_bf16_rne(x[2]) | (f32_to_bf16_rne(x[3]) << 16)};
       __builtin_amdgcn_raw_buffer_store_b64(w, r, voff, soff, kCachePolicyNT);
     } else {
-      const f32x4 x = {v.x, v.y, v.z, v.w};
-      __builtin_amdgcn_raw_buffer_store_b128(x, r, voff, soff, kCachePolicyNT);
+      const f32x4 w = {x[0], x[1], x[2], x[3]};
+      __builtin_amdgcn_raw_buffer_store_b128(w, r, voff, soff, kCachePolicyNT);
     }
   }
 };
@@ -332,6 +356,51 @@ __device__ __forceinline__ TokenScalars token_setup(const DecodeArgs& a, const T
   return s;
 }
 
+template <int N>
+constexpr int log2_exact() {
+  static_assert(N > 0 && (N & (N - 1)) == 0, "power of two");
+  int l = 0;
+  while ((1 << l) < N) ++l;
+  return l;
+}
+
+// ---------------------------------------------------------------------------
+// transpose-reduce over lane bits
+// ---------------------------------------------------------------------------
+
+// Exchange across lane bit BIT (partner lane ^ (1 << BIT)) with the cheapest
+// instruction for that bit: a row swap for bits 5 and 4, DPP below.  Lanes
+// with the bit clear keep `lo` + the partner's `lo`, the others `hi` + the
+// partner's `hi`; with lo == hi it is a plain pairwise sum.
+template <int BIT>
+__device__ __forceinline__ float xchg_level(bool up, float lo, float hi) {
+  if constexpr (BIT == 5) return swap32_add(lo, hi);
+  else if constexpr (BIT == 4) return swap16_add(lo, hi);
+  else return dpp_level<(1 << BIT)>(up, lo, hi);
+}
+
+// HALF-sized transpose levels on lane bits BIT, BIT-1, ...: each level keeps
+// half of the values a lane carries and sums it with the partner's copy, so
+// the last level leaves one value per lane.
+template <int HALF, int BIT>
+__device__ __forceinline__ void transpose_levels(float* vals, int lane) {
+  const bool up = ((lane >> BIT) & 1) != 0;
+#pragma unroll
+  for (int m = 0; m < HALF; ++m) vals[m] = xchg_level<BIT>(up, vals[m], vals[m + HALF]);
+  if constexpr (HALF > 1) transpose_levels<HALF / 2, BIT - 1>(vals, lane);
+}
+
+// Plain sums over lane bits HI down to LO (none when HI < LO).
+template <int HI, int LO>
+__device__ __forceinline__ float sum_levels(float x) {
+  if constexpr (HI >= LO) {
+    x = xchg_level<HI>(false, x, x);
+    return sum_levels<HI - 1, LO>(x);
+  } else {
+    return x;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // key-first layout: state [dk][dv]
 // ---------------------------------------------------------------------------
@@ -340,13 +409,20 @@ template <int DK, int DV, bool QBF16, bool SBF16>
 __global__ __launch_bounds__(kWave) void kda_decode_kfirst(const DecodeArgs a) {
   constexpr int CW = DV < 32 ? DV : 32;   // value columns of the wave's slab
   constexpr int SLABS = DV / CW;
-  constexpr int CQ = CW / 4;              // float4 column groups per slab
+  // values per lane and key row: 8 bf16 (one 16-byte access) for a bf16
+  // pool when dk has a row for each of the 64 / (CW / 8) row groups, else 4
+  constexpr int EPL = (SBF16 && DK >= kWave * 8 / CW) ? 8 : 4;
+  constexpr int CQ = CW / EPL;            // lanes across the slab's columns
   constexpr int RS = kWave / CQ;          // row groups across the wave
-  constexpr int R = DK / RS;              // rows per lane
+  constexpr int R = DK / RS;              // key rows per lane
+  constexpr int NV = 2 * EPL;             // partial sums per lane (a and b)
+  constexpr int LOG_CQ = log2_exact<CQ>();
+  constexpr int LOG_RS = log2_exact<RS>();
+  constexpr int LOG_NV = log2_exact<NV>();
   constexpr int CPL = DK >= 2 * kWave ? DK / kWave : 1;   // setup channels per lane
-  static_assert(DK % RS == 0 && R >= 1, "tile shape");
+  static_assert(DK % RS == 0 && R >= 1 && LOG_NV <= LOG_RS, "tile shape");
   static_assert(CPL * kWave >= DK && CPL <= 2, "setup split");
-  using IO = StateIO<SBF16>;
+  using IO = StateIO<SBF16, EPL>;
 
   __shared__ __attribute__((aligned(16))) float2 red_tab[2][DK];
   __shared__ __attribute__((aligned(16))) float2 upd_tab[2][DK];
@@ -362,7 +438,7 @@ __global__ __launch_bounds__(kWave) void kda_decode_kfirst(const DecodeArgs a) {
   }
   if (j.t0 == j.t1) return;
 
-  const int col0 = j.slab * CW + 4 * cq;
+  const int col0 = j.slab * CW + EPL * cq;
   const int c0 = lane * CPL;
   const bool chan_lane = c0 < DK;
   float dtb[CPL];
@@ -371,18 +447,22 @@ __global__ __launch_bounds__(kWave) void kda_decode_kfirst(const DecodeArgs a) {
   if (chan_lane) load_f32<CPL>(a.dt_bias + static_cast<int64_t>(j.hv) * DK + c0, dtb);
   const float amp = exp_f(a.a_log[j.hv]);
 
-  // state tile: one trip in
+  // state tile: one trip in; lane rows are rs + RS*i
   char* const tile = static_cast<char*>(a.state_pool) +
                      (static_cast<int64_t>(j.slot) * a.HV + j.hv) * (DK * DV * IO::kElem);
   const __amdgpu_buffer_rsrc_t res = tile_resource(tile, DK * DV * IO::kElem);
   const int voff = (rs * DV + col0) * IO::kElem;
   constexpr int kRowStep = RS * DV * IO::kElem;   // bytes between a lane's rows
-  float4 S[R];
+  float S[R][EPL];
 #pragma unroll
-  for (int i = 0; i < R; ++i) S[i] = IO::load(res, voff, i * kRowStep);
+  for (int i = 0; i < R; ++i) IO::load(res, voff, i * kRowStep, S[i]);
 
-  const bool holds_a = (rs & 4) == 0;          // after the reduction, see below
-  const int my_col = col0 + (rs & 3);
+  // After the reduction lane rs holds value m = rs & (NV-1): a[col0 + m] when
+  // m < EPL, else b[col0 + m - EPL]; row groups rs >= NV carry duplicates.
+  const int m_final = rs & (NV - 1);
+  const bool holds_a = m_final < EPL;
+  const bool owner = rs < NV;
+  const int my_col = col0 + (m_final & (EPL - 1));
 
   int buf = 0;
   for (int t = j.t0; t < j.t1; ++t, buf ^= 1) {
@@ -391,81 +471,45 @@ __global__ __launch_bounds__(kWave) void kda_decode_kfirst(const DecodeArgs a) {
     __syncthreads();
 
     // ---- one sweep: a = (kh*alpha)^T S, b = (qh*alpha)^T S, partial over rows ----
-    float acc[8];
+    float acc[NV];
 #pragma unroll
-    for (int m = 0; m < 8; ++m) acc[m] = 0.0f;
+    for (int m = 0; m < NV; ++m) acc[m] = 0.0f;
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       const float2 p = red_tab[buf][rs + RS * i];
-      acc[0] = fmaf(p.x, S[i].x, acc[0]);
-      acc[1] = fmaf(p.x, S[i].y, acc[1]);
-      acc[2] = fmaf(p.x, S[i].z, acc[2]);
-      acc[3] = fmaf(p.x, S[i].w, acc[3]);
-      acc[4] = fmaf(p.y, S[i].x, acc[4]);
-      acc[5] = fmaf(p.y, S[i].y, acc[5]);
-      acc[6] = fmaf(p.y, S[i].z, acc[6]);
-      acc[7] = fmaf(p.y, S[i].w, acc[7]);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        acc[e] = fmaf(p.x, S[i][e], acc[e]);
+        acc[EPL + e] = fmaf(p.y, S[i][e], acc[EPL + e]);
+      }
     }
 
-    // ---- transpose-reduce over the RS row-group lanes ----
-    // Lanes of a column group sit CQ apart.  Each butterfly level halves the
-    // values a lane carries, so after three levels lane rs holds value
-    // rs & 7: a[col0 + (rs&3)] when rs&4 == 0, else b[col0 + (rs&3)].
-    float red;
-    if constexpr (CQ == 8) {
-      // row-group bits are lane bits 5, 4, 3: two row swaps and one DPP move
-      float v4[4];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) v4[m] = swap32_add(acc[m], acc[m + 4]);
-      float v2[2];
-#pragma unroll
-      for (int m = 0; m < 2; ++m) v2[m] = swap16_add(v4[m], v4[m + 2]);
-      red = dpp_level<8>((rs & 1) != 0, v2[0], v2[1]);
-    } else {
-      float v4[4];
-      {
-        const bool up = (rs & 4) != 0;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const float send = up ? acc[m] : acc[m + 4];
-          const float keep = up ? acc[m + 4] : acc[m];
-          v4[m] = keep + __shfl_xor(send, 4 * CQ, kWave);
-        }
-      }
-      float v2[2];
-      {
-        const bool up = (rs & 2) != 0;
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          const float send = up ? v4[m] : v4[m + 2];
-          const float keep = up ? v4[m + 2] : v4[m];
-          v2[m] = keep + __shfl_xor(send, 2 * CQ, kWave);
-        }
-      }
-      const bool up = (rs & 1) != 0;
-      red = (up ? v2[1] : v2[0]) + __shfl_xor(up ? v2[0] : v2[1], CQ, kWave);
-#pragma unroll
-      for (int m = 8 * CQ; m < kWave; m <<= 1) red += __shfl_xor(red, m, kWave);
-    }
+    // ---- transpose-reduce over the RS row-group lanes (lane bits above LOG_CQ) ----
+    transpose_levels<NV / 2, LOG_CQ + LOG_NV - 1>(acc, lane);
+    const float red = sum_levels<LOG_CQ + LOG_RS - 1, LOG_CQ + LOG_NV>(acc[0]);
 
     // ---- u = v - a (to every lane of the column group); o = b + beta*(qh.kh)*u ----
-    if (holds_a && rs < 4) u_tab[4 * cq + rs] = v_mine - red;
+    if (holds_a && owner) u_tab[EPL * cq + m_final] = v_mine - red;
     __syncthreads();
-    const float4 u4 = *reinterpret_cast<const float4*>(&u_tab[4 * cq]);
-    if (!holds_a && rs < 8) {
-      const float uj = (rs & 2) ? ((rs & 1) ? u4.w : u4.z) : ((rs & 1) ? u4.y : u4.x);
-      store_scalar<QBF16>(a.out, (static_cast<int64_t>(t) * a.HV + j.hv) * DV + my_col,
-                          fmaf(ts.beta * ts.qk, uj, red));
+    float u[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; e += 4) {
+      const float4 x = *reinterpret_cast<const float4*>(&u_tab[EPL * cq + e]);
+      u[e] = x.x;
+      u[e + 1] = x.y;
+      u[e + 2] = x.z;
+      u[e + 3] = x.w;
     }
+    if (!holds_a && owner)
+      store_scalar<QBF16>(a.out, (static_cast<int64_t>(t) * a.HV + j.hv) * DV + my_col,
+                          fmaf(ts.beta * ts.qk, u[m_final & (EPL - 1)], red));
 
     // ---- S = alpha*S + (beta*kh) u^T ----
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       const float2 p = upd_tab[buf][rs + RS * i];
-      S[i].x = fmaf(p.y, u4.x, p.x * S[i].x);
-      S[i].y = fmaf(p.y, u4.y, p.x * S[i].y);
-      S[i].z = fmaf(p.y, u4.z, p.x * S[i].z);
-      S[i].w = fmaf(p.y, u4.w, p.x * S[i].w);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) S[i][e] = fmaf(p.y, u[e], p.x * S[i][e]);
     }
   }
 
@@ -478,19 +522,21 @@ __global__ __launch_bounds__(kWave) void kda_decode_kfirst(const DecodeArgs a) {
 // value-first layout: state [dv][dk]
 // ---------------------------------------------------------------------------
 
-template <int N>
-constexpr int log2_exact() {
-  static_assert(N > 0 && (N & (N - 1)) == 0, "power of two");
-  int l = 0;
-  while ((1 << l) < N) ++l;
-  return l;
-}
-
 template <int DK, int DV, bool QBF16, bool SBF16>
 __global__ __launch_bounds__(kWave) void kda_decode_vfirst(const DecodeArgs a) {
   constexpr int CW = DV < 32 ? DV : 32;   // value rows of the wave's slab
   constexpr int SLABS = DV / CW;
-  constexpr int KC = DK / 4;              // lanes across one row (4 keys each)
+  // keys per lane and value row: 8 when the slab has a row for each of the
+  // 512 / dk rows one load instruction then covers, else 4.  The 8 keys are
+  // two groups of 4: adjacent (one 16-byte access of 8 bf16) for a bf16 pool,
+  // dk/2 apart (two 16-byte fp32 accesses, each instruction reading half
+  // rows) for an fp32 pool.
+  constexpr int EPL = (kWave * 8 / DK <= CW) ? 8 : 4;
+  constexpr int Q = EPL / 4;              // 4-key groups per lane
+  constexpr bool ONE_ACCESS = SBF16 && EPL == 8;
+  constexpr int KSTEP = ONE_ACCESS ? 8 : 4;       // keys between neighbouring lanes
+  constexpr int QSTRIDE = ONE_ACCESS ? 4 : DK / 2;   // keys between a lane's groups
+  constexpr int KC = DK / EPL;            // lanes across one row
   constexpr int RPI = kWave / KC;         // rows per load instruction
   constexpr int L = CW / RPI;             // rows per lane
   constexpr int NV = 2 * L;               // partial sums per lane (a and b)
@@ -499,7 +545,7 @@ __global__ __launch_bounds__(kWave) void kda_decode_vfirst(const DecodeArgs a) {
   constexpr int CPL = DK >= 2 * kWave ? DK / kWave : 1;
   static_assert(L >= 1 && LOG_NV <= LOG_KC, "tile shape");
   static_assert(CPL * kWave >= DK && CPL <= 2, "setup split");
-  using IO = StateIO<SBF16>;
+  using IO = StateIO<SBF16, ONE_ACCESS ? 8 : 4>;
 
   __shared__ __attribute__((aligned(16))) float2 red_tab[2][DK];
   __shared__ __attribute__((aligned(16))) float2 upd_tab[2][DK];
@@ -523,16 +569,25 @@ __global__ __launch_bounds__(kWave) void kda_decode_vfirst(const DecodeArgs a) {
   if (chan_lane) load_f32<CPL>(a.dt_bias + static_cast<int64_t>(j.hv) * DK + c0, dtb);
   const float amp = exp_f(a.a_log[j.hv]);
 
-  // state tile: one trip in; lane rows are row0 + RPI*i
+  // state tile: one trip in; lane rows are row0 + RPI*i, keys key0 + QSTRIDE*q + 0..3
   const int row0 = j.slab * CW + rsub;
+  const int key0 = KSTEP * kc;
   char* const tile = static_cast<char*>(a.state_pool) +
                      (static_cast<int64_t>(j.slot) * a.HV + j.hv) * (DK * DV * IO::kElem);
   const __amdgpu_buffer_rsrc_t res = tile_resource(tile, DK * DV * IO::kElem);
-  const int voff = (row0 * DK + 4 * kc) * IO::kElem;
+  const int voff = (row0 * DK + key0) * IO::kElem;
   constexpr int kRowStep = RPI * DK * IO::kElem;
-  float4 S[L];
+  constexpr int kGroupStep = QSTRIDE * IO::kElem;
+  float S[L][EPL];
 #pragma unroll
-  for (int i = 0; i < L; ++i) S[i] = IO::load(res, voff, i * kRowStep);
+  for (int i = 0; i < L; ++i) {
+    if constexpr (ONE_ACCESS) {
+      IO::load(res, voff, i * kRowStep, S[i]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < Q; ++q) IO::load(res, voff + q * kGroupStep, i * kRowStep, &S[i][4 * q]);
+    }
+  }
 
   // After the reduction lane kc holds value m (see below): an a-value of
   // row i when m < L, else the b-value of row i = m - L.
@@ -548,49 +603,33 @@ __global__ __launch_bounds__(kWave) void kda_decode_vfirst(const DecodeArgs a) {
     const TokenScalars ts = token_setup<DK, CPL, QBF16>(a, j, t, c0, chan_lane, dtb, amp, red_tab[buf], upd_tab[buf]);
     __syncthreads();
 
-    // ---- sweep: per row, a and b partial over this lane's 4 keys ----
-    const float4 r01 = *reinterpret_cast<const float4*>(&red_tab[buf][4 * kc]);
-    const float4 r23 = *reinterpret_cast<const float4*>(&red_tab[buf][4 * kc + 2]);
+    // ---- sweep: per row, a and b partial over this lane's keys ----
+    float kq[EPL], qq[EPL];   // kh*alpha, qh*alpha of the lane's keys
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const float4 r01 = *reinterpret_cast<const float4*>(&red_tab[buf][key0 + QSTRIDE * q]);
+      const float4 r23 = *reinterpret_cast<const float4*>(&red_tab[buf][key0 + QSTRIDE * q + 2]);
+      kq[4 * q] = r01.x;  qq[4 * q] = r01.y;
+      kq[4 * q + 1] = r01.z;  qq[4 * q + 1] = r01.w;
+      kq[4 * q + 2] = r23.x;  qq[4 * q + 2] = r23.y;
+      kq[4 * q + 3] = r23.z;  qq[4 * q + 3] = r23.w;
+    }
     float vals[NV];
 #pragma unroll
     for (int i = 0; i < L; ++i) {
-      vals[i] = fmaf(r01.x, S[i].x, fmaf(r01.z, S[i].y, fmaf(r23.x, S[i].z, r23.z * S[i].w)));
-      vals[L + i] = fmaf(r01.y, S[i].x, fmaf(r01.w, S[i].y, fmaf(r23.y, S[i].z, r23.w * S[i].w)));
+      float sa = kq[0] * S[i][0], sb = qq[0] * S[i][0];
+#pragma unroll
+      for (int e = 1; e < EPL; ++e) {
+        sa = fmaf(kq[e], S[i][e], sa);
+        sb = fmaf(qq[e], S[i][e], sb);
+      }
+      vals[i] = sa;
+      vals[L + i] = sb;
     }
 
-    // ---- transpose-reduce over the KC lanes of a row ----
-    // Level s uses lane bit LOG_KC-1-s and halves the values a lane carries;
-    // lanes with the bit clear keep the lower half.  After LOG_NV levels a
-    // lane holds value m_final; remaining lane bits only add duplicates.
-    if constexpr (KC == 32 && NV == 32) {
-      // lane bits 4..0: one row swap, then DPP moves inside the row
-#pragma unroll
-      for (int m = 0; m < 16; ++m) vals[m] = swap16_add(vals[m], vals[m + 16]);
-      const bool b3 = (kc & 8) != 0, b2 = (kc & 4) != 0, b1 = (kc & 2) != 0, b0 = (kc & 1) != 0;
-#pragma unroll
-      for (int m = 0; m < 8; ++m) vals[m] = dpp_level<8>(b3, vals[m], vals[m + 8]);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) vals[m] = dpp_level<4>(b2, vals[m], vals[m + 4]);
-#pragma unroll
-      for (int m = 0; m < 2; ++m) vals[m] = dpp_level<2>(b1, vals[m], vals[m + 2]);
-      vals[0] = dpp_level<1>(b0, vals[0], vals[1]);
-    } else {
-#pragma unroll
-      for (int s = 0; s < LOG_NV; ++s) {
-        const int bit = LOG_KC - 1 - s;
-        const int half = NV >> (s + 1);
-        const bool up = ((kc >> bit) & 1) != 0;
-#pragma unroll
-        for (int m = 0; m < half; ++m) {
-          const float send = up ? vals[m] : vals[m + half];
-          const float keep = up ? vals[m + half] : vals[m];
-          vals[m] = keep + __shfl_xor(send, 1 << bit, kWave);
-        }
-      }
-#pragma unroll
-      for (int bit = LOG_KC - LOG_NV - 1; bit >= 0; --bit) vals[0] += __shfl_xor(vals[0], 1 << bit, kWave);
-    }
-    const float red = vals[0];
+    // ---- transpose-reduce over the KC lanes of a row (lane bits below LOG_KC) ----
+    transpose_levels<NV / 2, LOG_KC - 1>(vals, lane);
+    const float red = sum_levels<LOG_KC - LOG_NV - 1, 0>(vals[0]);
 
     // ---- u = v - a (to every lane of the row); o = b + beta*(qh.kh)*u ----
     if (holds_a && owner) u_tab[rsub * L + i_final] = v_mine - red;
@@ -600,20 +639,33 @@ __global__ __launch_bounds__(kWave) void kda_decode_vfirst(const DecodeArgs a) {
                           fmaf(ts.beta * ts.qk, u_tab[rsub * L + i_final], red));
 
     // ---- S = alpha*S + (beta*kh) u^T ----
-    const float4 p01 = *reinterpret_cast<const float4*>(&upd_tab[buf][4 * kc]);
-    const float4 p23 = *reinterpret_cast<const float4*>(&upd_tab[buf][4 * kc + 2]);
+    float al[EPL], bk[EPL];   // alpha, beta*kh of the lane's keys
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const float4 p01 = *reinterpret_cast<const float4*>(&upd_tab[buf][key0 + QSTRIDE * q]);
+      const float4 p23 = *reinterpret_cast<const float4*>(&upd_tab[buf][key0 + QSTRIDE * q + 2]);
+      al[4 * q] = p01.x;  bk[4 * q] = p01.y;
+      al[4 * q + 1] = p01.z;  bk[4 * q + 1] = p01.w;
+      al[4 * q + 2] = p23.x;  bk[4 * q + 2] = p23.y;
+      al[4 * q + 3] = p23.z;  bk[4 * q + 3] = p23.w;
+    }
 #pragma unroll
     for (int i = 0; i < L; ++i) {
       const float u = u_tab[rsub * L + i];
-      S[i].x = fmaf(p01.y, u, p01.x * S[i].x);
-      S[i].y = fmaf(p01.w, u, p01.z * S[i].y);
-      S[i].z = fmaf(p23.y, u, p23.x * S[i].z);
-      S[i].w = fmaf(p23.w, u, p23.z * S[i].w);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) S[i][e] = fmaf(bk[e], u, al[e] * S[i][e]);
     }
   }
 
 #pragma unroll
-  for (int i = 0; i < L; ++i) IO::store(res, voff, i * kRowStep, S[i]);
+  for (int i = 0; i < L; ++i) {
+    if constexpr (ONE_ACCESS) {
+      IO::store(res, voff, i * kRowStep, S[i]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < Q; ++q) IO::store(res, voff + q * kGroupStep, i * kRowStep, &S[i][4 * q]);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
