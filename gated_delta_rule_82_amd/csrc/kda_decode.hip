@@ -35,7 +35,8 @@
 // of the same request keep it in registers (fp32 even for a bf16 pool, which
 // is rounded to nearest-even once, on the way out).  Both trips carry the
 // nontemporal hint: the tile is touched once per call, and keeping it out of
-// L2 / MALL measurably raises the streaming rate.
+// L2 / MALL measurably raises the streaming rate.  (The key-first bf16 slab
+// is the exception: its rows are half cache lines, which L2 merges.)
 //
 // Workgroup order is XCD-aware: consecutive workgroup ids land on different
 // XCDs, so the id is remapped to give each XCD one contiguous range of
@@ -173,26 +174,26 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_resource(void* tile, int 
 // way in and rounded to nearest-even on the way out.
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-template <bool SBF16, int N>
+template <bool SBF16, int N, int POLICY = kCachePolicyNT>
 struct StateIO {
   static_assert(N == 4 || (SBF16 && N == 8), "state access width");
   static constexpr int kElem = SBF16 ? 2 : 4;
   __device__ static __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int voff, int soff, float* x) {
     if constexpr (SBF16 && N == 8) {
-      const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kCachePolicyNT);
+      const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, POLICY);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         x[2 * e] = bf16_to_f32(w[e] & 0xffffu);
         x[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
       }
     } else if constexpr (SBF16) {
-      const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kCachePolicyNT);
+      const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, POLICY);
       x[0] = bf16_to_f32(w.x & 0xffffu);
       x[1] = __uint_as_float(w.x & 0xffff0000u);
       x[2] = bf16_to_f32(w.y & 0xffffu);
       x[3] = __uint_as_float(w.y & 0xffff0000u);
     } else {
-      const f32x4 w = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kCachePolicyNT);
+      const f32x4 w = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, POLICY);
       x[0] = w.x;
       x[1] = w.y;
       x[2] = w.z;
@@ -204,14 +205,14 @@ struct StateIO {
       u32x4 w;
 #pragma unroll
       for (int e = 0; e < 4; ++e) w[e] = f32_to_bf16_rne(x[2 * e]) | (f32_to_bf16_rne(x[2 * e + 1]) << 16);
-      __builtin_amdgcn_raw_buffer_store_b128(w, r, voff, soff, kCachePolicyNT);
+      __builtin_amdgcn_raw_buffer_store_b128(w, r, voff, soff, POLICY);
     } else if constexpr (SBF16) {
       const u32x2 w = {f32_to_bf16_rne(x[0]) | (f32_to_bf16_rne(x[1]) << 16),
                        f32_to_bf16_rne(x[2]) | (f32_to_bf16_rne(x[3]) << 16)};
-      __builtin_amdgcn_raw_buffer_store_b64(w, r, voff, soff, kCachePolicyNT);
+      __builtin_amdgcn_raw_buffer_store_b64(w, r, voff, soff, POLICY);
     } else {
       const f32x4 w = {x[0], x[1], x[2], x[3]};
-      __builtin_amdgcn_raw_buffer_store_b128(w, r, voff, soff, kCachePolicyNT);
+      __builtin_amdgcn_raw_buffer_store_b128(w, r, voff, soff, POLICY);
     }
   }
 };
@@ -422,7 +423,11 @@ __global__ __launch_bounds__(kWave) void kda_decode_kfirst(const DecodeArgs a) {
   constexpr int CPL = DK >= 2 * kWave ? DK / kWave : 1;   // setup channels per lane
   static_assert(DK % RS == 0 && R >= 1 && LOG_NV <= LOG_RS, "tile shape");
   static_assert(CPL * kWave >= DK && CPL <= 2, "setup split");
-  using IO = StateIO<SBF16, EPL>;
+  // A bf16 slab row is 64 bytes, half a cache line shared with the next
+  // slab's wave: ordinary cached accesses let L2 merge the two halves
+  // (measured 341 us against 382 us with the nontemporal hint on the
+  // 96-head decode).  Full-line fp32 rows stream best with the hint.
+  using IO = StateIO<SBF16, EPL, (SBF16 && CW * 2 < 128) ? 0 : kCachePolicyNT>;
 
   __shared__ __attribute__((aligned(16))) float2 red_tab[2][DK];
   __shared__ __attribute__((aligned(16))) float2 upd_tab[2][DK];
