@@ -14,10 +14,13 @@ from .kda_oracle import (  # noqa: F401
     delta_write,
     gate,
     kda_decode,
+    kda_decode_conv,
     l2_normalize,
     read,
     round_to_bf16,
+    short_conv,
     sigmoid,
+    silu,
     softplus,
     write_strength,
 )

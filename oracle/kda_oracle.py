@@ -19,6 +19,12 @@ page title and section:
         ``dt_bias``, ``lower_bound``, ``scale`` and ``S``.
   [KDD] "KdaDecode" (Modular MAX Mojo builtin kernels): the default
         parameters (gate_mode, beta_mode, state_layout) and Tensor Shapes.
+  [TKG] also, for the short convolution in front of the recurrence: the
+        parameters conv_w (depthwise causal taps per q/k/v stream, tap 0 the
+        oldest position, tap-major), conv_state (the last K-1 pre-convolution
+        inputs per stream, read as the left part of the window and replaced by
+        the window ending at the newest token), the Background's "short
+        convolutions with SiLU", and Dimensions (K = 4 for Kimi K3).
 
 Readings taken where the pages are silent or ambiguous (each also listed in
 the design notes of the repository):
@@ -34,6 +40,11 @@ the design notes of the repository):
   * state dtype ([KDD] names state_dtype without its arithmetic): a bf16
     pool is read exactly, advanced in high precision through all of the
     request's tokens, and rounded to nearest-even when stored.
+  * short convolution: y_t = SiLU(sum_j w[j] * x_{t-K+1+j}) per channel with
+    no bias; windows are slotted like the state ([N, K-1, C], oldest first,
+    channels head-outer as in the q/k/v tensors); the convolved q, k, v are
+    handed to the recurrence in the activation dtype (the model's conv layer
+    returns them in it), i.e. rounded to nearest-even for bf16 inputs.
 
 Parity status: every function below is pinned by the CPU tests
 (``tests/test_oracle_pins.py``) against closed forms, hand-worked values,
@@ -290,3 +301,75 @@ def round_to_bf16(x):
     y = np.ldexp(np.rint(np.ldexp(xf, -quantum_exp)), quantum_exp)
     y = np.where(np.abs(y) > BF16_MAX, np.copysign(np.inf, y), y)
     return np.where(finite, y, x)
+
+
+# ----------------------------------------------------------------------------
+# the short causal convolution in front of the recurrence
+# ----------------------------------------------------------------------------
+
+def silu(x):
+    """SiLU(x) = x * sigmoid(x); [TKG] Background: short convolutions with SiLU."""
+    x = np.asarray(x, dtype=np.float64)
+    return x * sigmoid(x)
+
+
+def short_conv(x, window, w):
+    """Depthwise causal convolution of one request's inputs, then SiLU.
+
+    x [n, C] the request's new pre-convolution inputs in token order;
+    window [K-1, C] the K-1 inputs before them, oldest first ([TKG]
+    conv_state); w [K, C] the taps, tap 0 applied to the oldest position of
+    the window ([TKG] conv_w).  With xx = window followed by x,
+    y[t] = SiLU(sum_j w[j] * xx[t + j]) and the new window is the last K-1
+    rows of xx.  Returns (y [n, C], new window [K-1, C]) in fp64.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    window = np.asarray(window, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    K = w.shape[0]
+    xx = np.concatenate([window, x], axis=0)
+    n = x.shape[0]
+    y = np.zeros_like(x)
+    for t in range(n):
+        y[t] = silu(np.sum(w * xx[t:t + K], axis=0))
+    return y, xx[xx.shape[0] - (K - 1):]
+
+
+def kda_decode_conv(x_q, x_k, x_v, w_q, w_k, w_v, win_q, win_k, win_v, raw_gate,
+                    beta_logits, a_log, dt_bias, cu_seqlens, state_pool, state_indices, *,
+                    act_dtype="bf16", **decode_kw):
+    """The decode step with the short convolutions in front of the recurrence.
+
+    x_q, x_k [1, T, H, dk] and x_v [1, T, HV, dv] are the pre-convolution
+    projections; w_* [K, C] the taps with C = H*dk (q, k) or HV*dv (v),
+    channels head-outer; win_* [N, K-1, C] the slotted windows (slot
+    state_indices[b], like the recurrent state).  Per request, each stream
+    is convolved over its tokens (short_conv), rounded to the activation
+    dtype, and the recurrence (kda_decode) runs on the result.  A skipped
+    request (negative index) leaves its windows alone and gets zero q/k
+    rows; an empty request changes nothing.
+
+    Returns (out, state pool, win_q, win_k, win_v, q_conv, k_conv), the
+    windows as fp64 copies.
+    """
+    x = [np.asarray(a, dtype=np.float64)[0] for a in (x_q, x_k, x_v)]
+    w = [np.asarray(a, dtype=np.float64) for a in (w_q, w_k, w_v)]
+    win = [np.array(a, dtype=np.float64, copy=True) for a in (win_q, win_k, win_v)]
+    T = x[0].shape[0]
+    conv = [np.zeros_like(a) for a in x]
+    cu = [int(c) for c in np.asarray(cu_seqlens)]
+    idx = [int(i) for i in np.asarray(state_indices)]
+    for b, slot in enumerate(idx):
+        t0, t1 = cu[b], cu[b + 1]
+        if slot < 0 or t1 == t0:
+            continue
+        for s in range(3):
+            flat = x[s][t0:t1].reshape(t1 - t0, -1)
+            y, new_win = short_conv(flat, win[s][slot], w[s])
+            if act_dtype == "bf16":
+                y = round_to_bf16(y)
+            conv[s][t0:t1] = y.reshape(x[s][t0:t1].shape)
+            win[s][slot] = new_win
+    out, pool = kda_decode(conv[0][None], conv[1][None], conv[2][None], raw_gate, beta_logits,
+                           a_log, dt_bias, cu_seqlens, state_pool, state_indices, **decode_kw)
+    return out, pool, win[0], win[1], win[2], conv[0][None], conv[1][None]

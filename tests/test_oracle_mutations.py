@@ -21,6 +21,10 @@ def _all_pins():
         (pins.test_beta0_closed_form_decay, {}),
         (pins.test_orthonormal_keys_recall_exactly, {}),
         (pins.test_round_to_bf16_ties_and_library_agreement, {}),
+        (pins.test_silu_values, {}),
+        (pins.test_short_conv_matches_library_correlation, {}),
+        (pins.test_short_conv_tap_order_and_window_roll, {}),
+        (pins.test_decode_conv_windows_follow_requests, {}),
     ]
     for gm in (ko.GATE_SOFTPLUS, ko.GATE_LOWER_BOUND):
         for shape in ((3, 2, 4), (5, 7, 3), (1, 4, 2)):
@@ -59,6 +63,10 @@ MUTANTS = {
     "l2_no_sqrt": ("l2_normalize", lambda x, eps: np.asarray(x, np.float64) /
                    (np.sum(np.asarray(x, np.float64) ** 2, axis=-1, keepdims=True) + eps)),
     "bf16_round_half_up": ("round_to_bf16", None),
+    "conv_taps_reversed": ("short_conv", None),
+    "conv_window_not_rolled": ("short_conv", None),
+    "conv_without_silu": ("short_conv", None),
+    "silu_as_sigmoid": ("silu", lambda x: ko.sigmoid(x)),
 }
 
 
@@ -76,6 +84,22 @@ def _gate_mutant(kind):
             return orig(np.asarray(raw_gate) - 2 * np.asarray(dt_bias), dt_bias, a_log, gate_mode, lower_bound)
         return orig(raw_gate, dt_bias, a_log, gate_mode, lower_bound)
     return g
+
+
+def _conv_mutant(kind):
+    orig = ko.short_conv
+
+    def conv(x, window, w):
+        w = np.asarray(w, dtype=np.float64)
+        if kind == "conv_taps_reversed":
+            return orig(x, window, w[::-1])
+        y, new_win = orig(x, window, w)
+        if kind == "conv_window_not_rolled":
+            return y, np.asarray(window, dtype=np.float64)
+        xx = np.concatenate([np.asarray(window, np.float64), np.asarray(x, np.float64)])
+        raw = np.stack([np.sum(w * xx[t:t + w.shape[0]], axis=0) for t in range(len(x))])
+        return raw, new_win
+    return conv
 
 
 def _bf16_half_up(x):
@@ -96,5 +120,7 @@ def test_pins_catch_mutant(name, monkeypatch):
         fn = _gate_mutant(name)
     elif attr == "round_to_bf16":
         fn = _bf16_half_up
+    elif attr == "short_conv":
+        fn = _conv_mutant(name)
     monkeypatch.setattr(ko, attr, fn)
     assert _caught(), f"no pin catches mutant {name}"

@@ -411,3 +411,104 @@ def test_bf16_state_rounds_once_when_stored():
     assert np.array_equal(wl.bf16_bits_to_f32(bits).astype(np.float64), new_b)
     untouched = sorted(set(range(pool.shape[0])) - set(touched))
     assert np.array_equal(new_b[untouched], pool16[untouched])
+
+
+# ---------------------------------------------------------------------------
+# the short causal convolution in front of the recurrence
+# ---------------------------------------------------------------------------
+
+def test_silu_values():
+    x = np.linspace(-30, 30, 601)
+    np.testing.assert_allclose(ko.silu(x), x * scipy.special.expit(x), rtol=1e-14, atol=1e-300)
+    assert ko.silu(0.0) == 0.0
+    assert ko.silu(40.0) == pytest.approx(40.0, rel=1e-15)
+
+
+def test_short_conv_matches_library_correlation():
+    rng = _rng(30)
+    K, C, n = 4, 5, 6
+    x, win, w = rng.standard_normal((n, C)), rng.standard_normal((K - 1, C)), rng.standard_normal((K, C))
+    y, new_win = ko.short_conv(x, win, w)
+    xx = np.concatenate([win, x])
+    for c in range(C):
+        ref = np.correlate(xx[:, c], w[:, c], mode="valid")
+        np.testing.assert_allclose(y[:, c], ref * scipy.special.expit(ref), rtol=1e-13, atol=1e-15)
+    np.testing.assert_array_equal(new_win, x[-(K - 1):])
+
+
+def test_short_conv_tap_order_and_window_roll():
+    """Tap 0 multiplies the oldest position: an impulse at the first new token
+    meets tap K-1 first, then K-2, ...; short requests roll part of the old
+    window."""
+    K = 4
+    w = np.array([[1.0], [2.0], [3.0], [5.0]])
+    x = np.array([[1.0], [0.0], [0.0], [0.0], [0.0]])
+    y, _ = ko.short_conv(x, np.zeros((K - 1, 1)), w)
+    np.testing.assert_allclose(y[:, 0], ko.silu(np.array([5.0, 3.0, 2.0, 1.0, 0.0])), rtol=1e-15)
+    win = np.array([[7.0], [8.0], [9.0]])
+    _, roll1 = ko.short_conv(np.array([[4.0]]), win, w)
+    np.testing.assert_array_equal(roll1[:, 0], [8.0, 9.0, 4.0])
+    y1, roll2 = ko.short_conv(np.array([[4.0], [6.0]]), win, w)
+    np.testing.assert_array_equal(roll2[:, 0], [9.0, 4.0, 6.0])
+    # first output: 1*7 + 2*8 + 3*9 + 5*4 = 70
+    assert y1[0, 0] == pytest.approx(70.0, rel=1e-15)
+
+
+def test_short_conv_split_invariance():
+    rng = _rng(31)
+    K, C, n = 4, 3, 7
+    x, win, w = rng.standard_normal((n, C)), rng.standard_normal((K - 1, C)), rng.standard_normal((K, C))
+    y_all, win_all = ko.short_conv(x, win, w)
+    cur = win
+    for t in range(n):
+        y_t, cur = ko.short_conv(x[t:t + 1], cur, w)
+        assert np.array_equal(y_t[0], y_all[t])
+    assert np.array_equal(cur, win_all)
+
+
+def _conv_batch(seed=32, B=3, H=2, HV=4, dk=8, dv=6, counts=(2, 0, 3), slots=6, K=4, idx=None):
+    d, cu, pool, idx0 = _small_batch(seed=seed, B=B, H=H, HV=HV, dk=dk, dv=dv, counts=counts, slots=slots)
+    rng = _rng(seed + 100)
+    T = int(cu[-1])
+    xs = dict(x_q=rng.standard_normal((1, T, H, dk)), x_k=rng.standard_normal((1, T, H, dk)),
+              x_v=rng.standard_normal((1, T, HV, dv)))
+    ws = dict(w_q=rng.standard_normal((K, H * dk)) * 0.5, w_k=rng.standard_normal((K, H * dk)) * 0.5,
+              w_v=rng.standard_normal((K, HV * dv)) * 0.5)
+    wins = dict(win_q=rng.standard_normal((slots, K - 1, H * dk)), win_k=rng.standard_normal((slots, K - 1, H * dk)),
+                win_v=rng.standard_normal((slots, K - 1, HV * dv)))
+    rest = {k_: v_ for k_, v_ in d.items() if k_ not in ("q", "k", "v")}
+    return xs, ws, wins, rest, cu, pool, (idx0 if idx is None else np.asarray(idx, dtype=np.int32))
+
+
+def test_decode_conv_wires_the_convolution_into_the_recurrence():
+    """Taps (0, 0, 0, 1) make every stream SiLU(x): the decode step then equals
+    the plain recurrence on SiLU(x) rounded to the activation dtype."""
+    xs, ws, wins, rest, cu, pool, idx = _conv_batch()
+    for key in ws:
+        ws[key][:] = 0.0
+        ws[key][-1] = 1.0
+    out, new_pool, wq, wk, wv, qc, kc = ko.kda_decode_conv(
+        **xs, **ws, **wins, **rest, cu_seqlens=cu, state_pool=pool, state_indices=idx)
+    sx = {k_: ko.round_to_bf16(ko.silu(v_)) for k_, v_ in xs.items()}
+    # skipped / empty requests get zero q/k rows in the convolved tensors
+    out_ref, pool_ref = ko.kda_decode(sx["x_q"], sx["x_k"], sx["x_v"], **rest, cu_seqlens=cu,
+                                      state_pool=pool, state_indices=idx)
+    np.testing.assert_allclose(out, out_ref, rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(new_pool, pool_ref, rtol=1e-14, atol=1e-15)
+    np.testing.assert_array_equal(qc, sx["x_q"])
+    np.testing.assert_array_equal(kc, sx["x_k"])
+
+
+def test_decode_conv_windows_follow_requests():
+    """Each request's windows move by its own tokens, in its own slot; empty
+    and skipped requests leave their windows alone."""
+    xs, ws, wins, rest, cu, pool, idx = _conv_batch(counts=(2, 0, 3), idx=[4, 1, -1])
+    out, new_pool, wq, wk, wv, qc, kc = ko.kda_decode_conv(
+        **xs, **ws, **wins, **rest, cu_seqlens=cu, state_pool=pool, state_indices=idx)
+    untouched = [0, 1, 2, 3, 5]                 # slot 1 empty request, request 2 skipped
+    for new, old in ((wq, wins["win_q"]), (wk, wins["win_k"]), (wv, wins["win_v"])):
+        assert np.array_equal(new[untouched], old[untouched])
+    # request 0 (2 tokens, K - 1 = 3): window = [old[-1], x0, x1]
+    xq = xs["x_q"][0].reshape(cu[-1], -1)
+    np.testing.assert_array_equal(wq[4], np.concatenate([wins["win_q"][4][-1:], xq[0:2]]))
+    assert np.all(qc[0, 2:5] == 0.0) and np.all(out[0, 2:5] == 0.0)
