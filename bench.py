@@ -151,6 +151,8 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default=None)
     ap.add_argument("--state-layout", choices=("k_first", "v_first"), default="k_first")
     ap.add_argument("--state-dtype", choices=("f32", "bf16"), default="f32")
+    ap.add_argument("--conv", action="store_true",
+                    help="time kda_decode_conv: the step with the short convolutions in front")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for cpu_baseline (0 disables)")
     ap.add_argument("--no-copy-ceiling", action="store_true")
@@ -189,10 +191,23 @@ def main(argv=None) -> int:
     handle = stream.cuda_stream
     mode = dict(gate_mode=cfg.gate_mode, lower_bound=cfg.lower_bound, state_layout=cfg.state_layout)
 
-    def step():
-        kda.decode(out, dev["q"], dev["k"], dev["v"], dev["raw_gate"], dev["beta_logits"],
-                   dev["a_log"], dev["dt_bias"], dev["cu_seqlens"], pool, dev["state_indices"],
-                   stream=handle, **mode)
+    if args.conv:
+        ci = wl.draw_conv(inp)
+        cd = wl.conv_to_device(ci, cfg.qkv_dtype)
+        conv_bytes = wl.conv_bytes(cfg, inp, ci.K)
+        alg_bytes += conv_bytes
+        torch.cuda.synchronize()
+
+        def step():
+            kda.decode_conv(out, cd["x_q"], cd["x_k"], cd["x_v"], cd["w_q"], cd["w_k"], cd["w_v"],
+                            cd["win_q"], cd["win_k"], cd["win_v"], cd["q_conv"], cd["k_conv"],
+                            dev["raw_gate"], dev["beta_logits"], dev["a_log"], dev["dt_bias"],
+                            dev["cu_seqlens"], pool, dev["state_indices"], stream=handle, **mode)
+    else:
+        def step():
+            kda.decode(out, dev["q"], dev["k"], dev["v"], dev["raw_gate"], dev["beta_logits"],
+                       dev["a_log"], dev["dt_bias"], dev["cu_seqlens"], pool, dev["state_indices"],
+                       stream=handle, **mode)
 
     for _ in range(args.warmup):
         step()
@@ -219,6 +234,8 @@ def main(argv=None) -> int:
     achieved = alg_bytes / (mean_kernel_ms * 1e-3) / 1e9
     variant = "" if (cfg.state_layout, cfg.state_dtype) == ("k_first", "f32") else \
         f"_{cfg.state_layout}_{cfg.state_dtype}"
+    if args.conv:
+        variant += "_conv"
     traffic, traffic_src = committed_traffic(name + variant)
     log(f"[bench] traffic: {traffic} ({traffic_src})")
 
@@ -231,7 +248,7 @@ def main(argv=None) -> int:
     cpu = None
     if args.cpu_budget > 0:
         log(f"[bench] cpu_baseline: oracle for ~{args.cpu_budget:.0f} s")
-        cpu = cpu_baseline(inp, pool, args.cpu_budget)
+        cpu = cpu_baseline(inp, pool, args.cpu_budget) if not args.conv else None
         log(f"[bench] cpu_baseline {cpu['value']} GB/s, {cpu['tokens_heads_per_s']} token-heads/s")
 
     counts = np.diff(inp.cu_seqlens)
@@ -253,6 +270,7 @@ def main(argv=None) -> int:
             "tokens_per_request": cfg.tokens, "total_tokens": inp.T,
             "qkv_dtype": cfg.qkv_dtype, "state_dtype": cfg.state_dtype,
             "state_layout": cfg.state_layout, "gate": cfg.gate_mode,
+            "short_conv": bool(args.conv),
             "slots": cfg.n_slots, "parallelism": "single GPU",
         },
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),

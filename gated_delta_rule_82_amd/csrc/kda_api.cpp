@@ -83,12 +83,25 @@ int kda_check_host(const int32_t* cu_seqlens, const int32_t* state_indices, int6
   return KDA_OK;
 }
 
-int kda_decode(const kda_tensor* out, const kda_tensor* q, const kda_tensor* k,
-               const kda_tensor* v, const kda_tensor* raw_gate,
-               const kda_tensor* beta_logits, const kda_tensor* a_log,
-               const kda_tensor* dt_bias, const kda_tensor* cu_seqlens,
-               const kda_tensor* state_pool, const kda_tensor* state_indices,
-               const kda_mode* mode, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Every check of a decode call; fills `args` and the launch selectors.
+// Returns KDA_OK or the first error; touches no device state.
+struct Plan {
+  kda::DecodeArgs args;
+  int dk, dv;
+  bool qkv_bf16, state_bf16, empty;
+  int layout;
+};
+
+int plan_decode(const kda_tensor* out, const kda_tensor* q, const kda_tensor* k,
+                const kda_tensor* v, const kda_tensor* raw_gate,
+                const kda_tensor* beta_logits, const kda_tensor* a_log,
+                const kda_tensor* dt_bias, const kda_tensor* cu_seqlens,
+                const kda_tensor* state_pool, const kda_tensor* state_indices,
+                const kda_mode* mode, Plan* plan, bool qk_f32 = false) {
   if (mode == nullptr) return KDA_ERR_NULL;
   KDA_TRY(check_tensor(out, 4));
   KDA_TRY(check_tensor(q, 4));
@@ -102,10 +115,12 @@ int kda_decode(const kda_tensor* out, const kda_tensor* q, const kda_tensor* k,
   KDA_TRY(check_tensor(state_pool, 4));
   KDA_TRY(check_tensor(state_indices, 1));
 
-  // dtypes: q, k, v share bf16 or f32; out follows v; the rest are fixed
+  // dtypes: q, k, v share bf16 or f32 (q, k are f32 when qk_f32); out
+  // follows v; the rest are fixed
   const int32_t qkv = v->dtype;
+  const int32_t qk = qk_f32 ? KDA_F32 : qkv;
   if (qkv != KDA_BF16 && qkv != KDA_F32) return KDA_ERR_DTYPE;
-  if (q->dtype != qkv || k->dtype != qkv || out->dtype != qkv) return KDA_ERR_DTYPE;
+  if (q->dtype != qk || k->dtype != qk || out->dtype != qkv) return KDA_ERR_DTYPE;
   if (raw_gate->dtype != KDA_F32 || beta_logits->dtype != KDA_F32 || a_log->dtype != KDA_F32 ||
       dt_bias->dtype != KDA_F32)
     return KDA_ERR_DTYPE;
@@ -157,9 +172,9 @@ int kda_decode(const kda_tensor* out, const kda_tensor* q, const kda_tensor* k,
   if (!(std::isfinite(mode->l2_eps) && mode->l2_eps >= 0.0f)) return KDA_ERR_MODE;
   if (!(std::isfinite(mode->scale) && mode->scale >= 0.0f)) return KDA_ERR_MODE;
 
-  if (B == 0 || T == 0) return KDA_OK;   // nothing to advance and no output row
-
-  kda::DecodeArgs args;
+  plan->empty = B == 0 || T == 0;   // nothing to advance and no output row
+  kda::DecodeArgs& args = plan->args;
+  args = kda::DecodeArgs{};
   args.out = out->data;
   args.q = q->data;
   args.k = k->data;
@@ -181,8 +196,107 @@ int kda_decode(const kda_tensor* out, const kda_tensor* q, const kda_tensor* k,
   args.lower_bound = mode->gate_mode == KDA_GATE_LOWER_BOUND ? mode->lower_bound : 0.0f;
   args.l2_eps = mode->l2_eps == 0.0f ? 1e-6f : mode->l2_eps;
   args.scale = mode->scale == 0.0f ? 1.0f / std::sqrt(static_cast<float>(DK)) : mode->scale;
-  return kda::launch_decode(args, static_cast<int>(DK), static_cast<int>(DV), qkv == KDA_BF16,
-                            state_pool->dtype == KDA_BF16, mode->state_layout, stream);
+  plan->dk = static_cast<int>(DK);
+  plan->dv = static_cast<int>(DV);
+  plan->qkv_bf16 = qkv == KDA_BF16;
+  plan->state_bf16 = state_pool->dtype == KDA_BF16;
+  plan->layout = mode->state_layout;
+  return KDA_OK;
+}
+
+
+}  // namespace
+
+extern "C" {
+
+int kda_decode(const kda_tensor* out, const kda_tensor* q, const kda_tensor* k,
+               const kda_tensor* v, const kda_tensor* raw_gate,
+               const kda_tensor* beta_logits, const kda_tensor* a_log,
+               const kda_tensor* dt_bias, const kda_tensor* cu_seqlens,
+               const kda_tensor* state_pool, const kda_tensor* state_indices,
+               const kda_mode* mode, hipStream_t stream) {
+  Plan plan;
+  KDA_TRY(plan_decode(out, q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens,
+                      state_pool, state_indices, mode, &plan));
+  if (plan.empty) return KDA_OK;
+  return kda::launch_decode(plan.args, plan.dk, plan.dv, plan.qkv_bf16, plan.state_bf16,
+                            plan.layout, false, stream);
+}
+
+int kda_decode_conv(const kda_tensor* out, const kda_conv* conv, const kda_tensor* raw_gate,
+                    const kda_tensor* beta_logits, const kda_tensor* a_log,
+                    const kda_tensor* dt_bias, const kda_tensor* cu_seqlens,
+                    const kda_tensor* state_pool, const kda_tensor* state_indices,
+                    const kda_mode* mode, hipStream_t stream) {
+  if (conv == nullptr) return KDA_ERR_NULL;
+  // the recurrence sees q = q_conv, k = k_conv and v shaped like x_v
+  Plan plan;
+  KDA_TRY(plan_decode(out, &conv->q_conv, &conv->k_conv, &conv->x_v, raw_gate, beta_logits,
+                      a_log, dt_bias, cu_seqlens, state_pool, state_indices, mode, &plan,
+                      /*qk_f32=*/true));
+  const kda::DecodeArgs& d = plan.args;
+  const int64_t T = d.T, H = conv->q_conv.shape[2], HV = conv->x_v.shape[2];
+  const int64_t DK = plan.dk, DV = plan.dv, N = state_pool->shape[0];
+  KDA_TRY(check_tensor(&conv->x_q, 4));
+  KDA_TRY(check_tensor(&conv->x_k, 4));
+  KDA_TRY(check_tensor(&conv->w_q, 2));
+  KDA_TRY(check_tensor(&conv->w_k, 2));
+  KDA_TRY(check_tensor(&conv->w_v, 2));
+  KDA_TRY(check_tensor(&conv->win_q, 3));
+  KDA_TRY(check_tensor(&conv->win_k, 3));
+  KDA_TRY(check_tensor(&conv->win_v, 3));
+  const int32_t act = conv->x_v.dtype;
+  if (conv->x_q.dtype != act || conv->x_k.dtype != act) return KDA_ERR_DTYPE;
+  const int32_t wdt = conv->w_q.dtype;
+  if ((wdt != KDA_F32 && wdt != KDA_BF16) || conv->w_k.dtype != wdt || conv->w_v.dtype != wdt)
+    return KDA_ERR_DTYPE;
+  if (conv->win_q.dtype != KDA_F32 || conv->win_k.dtype != KDA_F32 || conv->win_v.dtype != KDA_F32)
+    return KDA_ERR_DTYPE;
+  for (int i = 0; i < 4; ++i)
+    if (conv->x_q.shape[i] != conv->q_conv.shape[i] || conv->x_k.shape[i] != conv->q_conv.shape[i])
+      return KDA_ERR_SHAPE;
+  const int64_t K = conv->w_q.shape[0];
+  const int64_t CQ = H * DK, CV = HV * DV;
+  if (conv->w_q.shape[1] != CQ || conv->w_k.shape[0] != K || conv->w_k.shape[1] != CQ ||
+      conv->w_v.shape[0] != K || conv->w_v.shape[1] != CV)
+    return KDA_ERR_SHAPE;
+  const kda_tensor* wins[3] = {&conv->win_q, &conv->win_k, &conv->win_v};
+  for (int s = 0; s < 3; ++s)
+    if (wins[s]->shape[0] != N || wins[s]->shape[1] != K - 1 || wins[s]->shape[2] != (s < 2 ? CQ : CV))
+      return KDA_ERR_SHAPE;
+  if (K < 2 || K > 4) return KDA_ERR_UNSUPPORTED;
+  const kda_tensor* extra[] = {&conv->x_q, &conv->x_k, &conv->w_q, &conv->w_k, &conv->w_v,
+                               &conv->win_q, &conv->win_k, &conv->win_v};
+  for (const kda_tensor* t : extra)
+    if (!aligned(t, 16)) return KDA_ERR_UNSUPPORTED;
+  if (plan.empty) return KDA_OK;
+
+  kda::ConvQKArgs c{};
+  c.x[0] = conv->x_q.data;
+  c.x[1] = conv->x_k.data;
+  c.w[0] = conv->w_q.data;
+  c.w[1] = conv->w_k.data;
+  c.win[0] = static_cast<float*>(conv->win_q.data);
+  c.win[1] = static_cast<float*>(conv->win_k.data);
+  c.y[0] = conv->q_conv.data;
+  c.y[1] = conv->k_conv.data;
+  c.cu_seqlens = d.cu_seqlens;
+  c.state_indices = d.state_indices;
+  c.B = d.B;
+  c.T = static_cast<int32_t>(T);
+  c.H = static_cast<int32_t>(H);
+  c.N = d.N;
+  c.conv_k = static_cast<int32_t>(K);
+  c.w_bf16 = wdt == KDA_BF16;
+  KDA_TRY(kda::launch_conv_qk(c, plan.dk, act == KDA_BF16, stream));
+
+  kda::DecodeArgs args = plan.args;
+  args.conv_w_v = conv->w_v.data;
+  args.conv_win_v = static_cast<float*>(conv->win_v.data);
+  args.conv_k = static_cast<int32_t>(K);
+  args.conv_w_bf16 = wdt == KDA_BF16;
+  return kda::launch_decode(args, plan.dk, plan.dv, plan.qkv_bf16, plan.state_bf16, plan.layout,
+                            true, stream);
 }
 
 }  // extern "C"

@@ -366,6 +366,100 @@ constexpr int log2_exact() {
 }
 
 // ---------------------------------------------------------------------------
+// short causal convolution (the step in front of the recurrence)
+// ---------------------------------------------------------------------------
+
+constexpr int kMaxConvK = 4;
+
+__device__ __forceinline__ float silu_f(float x) { return x * sigmoid_f(x); }
+
+__device__ __forceinline__ float load_tap(const void* w, int64_t off, bool bf16) {
+  return bf16 ? bf16_to_f32(static_cast<const uint16_t*>(w)[off]) : static_cast<const float*>(w)[off];
+}
+
+// One channel's convolution carried through a request's tokens in
+// registers: the K-1 previous pre-convolution inputs (oldest first) and the
+// K taps (tap 0 meets the oldest position).  Window [N, K-1, C], taps [K, C].
+struct ConvChannel {
+  float win[kMaxConvK - 1];
+  float tap[kMaxConvK];
+
+  __device__ __forceinline__ void load(const void* w, const float* window, int64_t slot, int64_t C,
+                                       int64_t ch, int K, bool w_bf16) {
+#pragma unroll
+    for (int q = 0; q < kMaxConvK; ++q) tap[q] = q < K ? load_tap(w, q * C + ch, w_bf16) : 0.0f;
+#pragma unroll
+    for (int q = 0; q < kMaxConvK - 1; ++q) win[q] = q < K - 1 ? window[(slot * (K - 1) + q) * C + ch] : 0.0f;
+  }
+
+  // Convolve the next input x, roll the window, return SiLU of the sum
+  // (fp32, unrounded).  (Register arrays are only indexed by compile-time
+  // positions; K selects.)
+  __device__ __forceinline__ float step(float x, int K) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int q = 0; q < kMaxConvK; ++q) {
+      const float in = q < K - 1 ? win[q < kMaxConvK - 1 ? q : 0] : x;   // window position q
+      if (q < K) acc = fmaf(tap[q], in, acc);
+    }
+#pragma unroll
+    for (int q = 0; q < kMaxConvK - 1; ++q) {
+      const float next = q + 1 < kMaxConvK - 1 ? win[q + 1 < kMaxConvK - 1 ? q + 1 : 0] : x;
+      win[q] = q < K - 2 ? next : (q == K - 2 ? x : win[q]);
+    }
+    return silu_f(acc);
+  }
+
+  __device__ __forceinline__ void store(float* window, int64_t slot, int64_t C, int64_t ch, int K) const {
+#pragma unroll
+    for (int q = 0; q < kMaxConvK - 1; ++q)
+      if (q < K - 1) window[(slot * (K - 1) + q) * C + ch] = win[q];
+  }
+};
+
+// q and k of every (request, key head): one workgroup per (request, key
+// head, stream), CPL channels per lane, fp32 results.  A lane reads and
+// writes only its own channels' windows, so the in-place window update needs
+// no ordering.
+template <int DK, bool XBF16>
+__global__ __launch_bounds__(kWave) void kda_conv_qk(const ConvQKArgs a) {
+  constexpr int CPL = DK >= 2 * kWave ? DK / kWave : 1;
+  const int lane = threadIdx.x;
+  const int s = static_cast<int>(blockIdx.x % 2);
+  const int bh = static_cast<int>(blockIdx.x / 2);
+  const int b = bh / a.H;
+  const int h = bh - b * a.H;
+  int t0 = a.cu_seqlens[b];
+  int t1 = a.cu_seqlens[b + 1];
+  t0 = t0 < 0 ? 0 : (t0 > a.T ? a.T : t0);
+  t1 = t1 < t0 ? t0 : (t1 > a.T ? a.T : t1);
+  const int slot = a.state_indices[b];
+  const int c0 = lane * CPL;
+  if (c0 >= DK) return;
+  const int64_t C = static_cast<int64_t>(a.H) * DK;
+  const int64_t ch = static_cast<int64_t>(h) * DK + c0;
+  if (slot < 0 || slot >= a.N) {
+    for (int t = t0; t < t1; ++t)
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) store_scalar<false>(a.y[s], static_cast<int64_t>(t) * C + ch + c, 0.0f);
+    return;
+  }
+  if (t0 == t1) return;
+  ConvChannel cv[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) cv[c].load(a.w[s], a.win[s], slot, C, ch + c, a.conv_k, a.w_bf16 != 0);
+  for (int t = t0; t < t1; ++t) {
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int64_t off = static_cast<int64_t>(t) * C + ch + c;
+      store_scalar<false>(a.y[s], off, cv[c].step(load_scalar<XBF16>(a.x[s], off), a.conv_k));
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) cv[c].store(a.win[s], slot, C, ch + c, a.conv_k);
+}
+
+// ---------------------------------------------------------------------------
 // transpose-reduce over lane bits
 // ---------------------------------------------------------------------------
 
@@ -406,7 +500,7 @@ __device__ __forceinline__ float sum_levels(float x) {
 // key-first layout: state [dk][dv]
 // ---------------------------------------------------------------------------
 
-template <int DK, int DV, bool QBF16, bool SBF16>
+template <int DK, int DV, bool QBF16, bool SBF16, bool CONVV>
 __global__ __launch_bounds__(kWave) void kda_decode_kfirst(const DecodeArgs a) {
   constexpr int CW = DV < 32 ? DV : 32;   // value columns of the wave's slab
   constexpr int SLABS = DV / CW;
@@ -469,10 +563,20 @@ __global__ __launch_bounds__(kWave) void kda_decode_kfirst(const DecodeArgs a) {
   const bool owner = rs < NV;
   const int my_col = col0 + (m_final & (EPL - 1));
 
+  // with the convolution in front, the a-lanes convolve their v channel
+  const int64_t v_ch = static_cast<int64_t>(j.hv) * DV + my_col;
+  ConvChannel cv;
+  if constexpr (CONVV)
+    if (holds_a) cv.load(a.conv_w_v, a.conv_win_v, j.slot, static_cast<int64_t>(a.HV) * DV, v_ch, a.conv_k, a.conv_w_bf16 != 0);
+
   int buf = 0;
   for (int t = j.t0; t < j.t1; ++t, buf ^= 1) {
-    const float v_mine = holds_a ? load_scalar<QBF16>(a.v, (static_cast<int64_t>(t) * a.HV + j.hv) * DV + my_col) : 0.0f;
-    const TokenScalars ts = token_setup<DK, CPL, QBF16>(a, j, t, c0, chan_lane, dtb, amp, red_tab[buf], upd_tab[buf]);
+    float v_mine = holds_a ? load_scalar<QBF16>(a.v, static_cast<int64_t>(t) * a.HV * DV + v_ch) : 0.0f;
+    if constexpr (CONVV)
+      if (holds_a) v_mine = cv.step(v_mine, a.conv_k);
+    // with the convolution in front, q and k arrive convolved in fp32
+    const TokenScalars ts = token_setup<DK, CPL, QBF16 && !CONVV>(a, j, t, c0, chan_lane, dtb, amp,
+                                                                red_tab[buf], upd_tab[buf]);
     __syncthreads();
 
     // ---- one sweep: a = (kh*alpha)^T S, b = (qh*alpha)^T S, partial over rows ----
@@ -521,13 +625,15 @@ __global__ __launch_bounds__(kWave) void kda_decode_kfirst(const DecodeArgs a) {
   // state tile: one trip out, to the same slot
 #pragma unroll
   for (int i = 0; i < R; ++i) IO::store(res, voff, i * kRowStep, S[i]);
+  if constexpr (CONVV)
+    if (holds_a && owner) cv.store(a.conv_win_v, j.slot, static_cast<int64_t>(a.HV) * DV, v_ch, a.conv_k);
 }
 
 // ---------------------------------------------------------------------------
 // value-first layout: state [dv][dk]
 // ---------------------------------------------------------------------------
 
-template <int DK, int DV, bool QBF16, bool SBF16>
+template <int DK, int DV, bool QBF16, bool SBF16, bool CONVV>
 __global__ __launch_bounds__(kWave) void kda_decode_vfirst(const DecodeArgs a) {
   constexpr int CW = DV < 32 ? DV : 32;   // value rows of the wave's slab
   constexpr int SLABS = DV / CW;
@@ -602,10 +708,20 @@ __global__ __launch_bounds__(kWave) void kda_decode_vfirst(const DecodeArgs a) {
   const bool owner = (kc & ((1 << (LOG_KC - LOG_NV)) - 1)) == 0;   // not a duplicate
   const int my_row = row0 + RPI * i_final;
 
+  // with the convolution in front, the a-lanes convolve their v channel
+  const int64_t v_ch = static_cast<int64_t>(j.hv) * DV + my_row;
+  ConvChannel cv;
+  if constexpr (CONVV)
+    if (holds_a) cv.load(a.conv_w_v, a.conv_win_v, j.slot, static_cast<int64_t>(a.HV) * DV, v_ch, a.conv_k, a.conv_w_bf16 != 0);
+
   int buf = 0;
   for (int t = j.t0; t < j.t1; ++t, buf ^= 1) {
-    const float v_mine = holds_a ? load_scalar<QBF16>(a.v, (static_cast<int64_t>(t) * a.HV + j.hv) * DV + my_row) : 0.0f;
-    const TokenScalars ts = token_setup<DK, CPL, QBF16>(a, j, t, c0, chan_lane, dtb, amp, red_tab[buf], upd_tab[buf]);
+    float v_mine = holds_a ? load_scalar<QBF16>(a.v, static_cast<int64_t>(t) * a.HV * DV + v_ch) : 0.0f;
+    if constexpr (CONVV)
+      if (holds_a) v_mine = cv.step(v_mine, a.conv_k);
+    // with the convolution in front, q and k arrive convolved in fp32
+    const TokenScalars ts = token_setup<DK, CPL, QBF16 && !CONVV>(a, j, t, c0, chan_lane, dtb, amp,
+                                                                red_tab[buf], upd_tab[buf]);
     __syncthreads();
 
     // ---- sweep: per row, a and b partial over this lane's keys ----
@@ -671,61 +787,86 @@ __global__ __launch_bounds__(kWave) void kda_decode_vfirst(const DecodeArgs a) {
       for (int q = 0; q < Q; ++q) IO::store(res, voff + q * kGroupStep, i * kRowStep, &S[i][4 * q]);
     }
   }
+  if constexpr (CONVV)
+    if (holds_a && owner) cv.store(a.conv_win_v, j.slot, static_cast<int64_t>(a.HV) * DV, v_ch, a.conv_k);
 }
 
 // ---------------------------------------------------------------------------
 // dispatch
 // ---------------------------------------------------------------------------
 
-template <int DK, int DV, bool QBF16, bool SBF16, int LAYOUT>
+template <int DK, int DV, bool QBF16, bool SBF16, int LAYOUT, bool CONVV>
 hipError_t launch_one(const DecodeArgs& args, hipStream_t stream) {
   constexpr int CW = DV < 32 ? DV : 32;
   const int64_t nwg = static_cast<int64_t>(args.B) * args.HV * (DV / CW);
   void* kargs[] = {const_cast<DecodeArgs*>(&args)};
   const void* fn = LAYOUT == KDA_STATE_K_FIRST
-                       ? reinterpret_cast<const void*>(&kda_decode_kfirst<DK, DV, QBF16, SBF16>)
-                       : reinterpret_cast<const void*>(&kda_decode_vfirst<DK, DV, QBF16, SBF16>);
+                       ? reinterpret_cast<const void*>(&kda_decode_kfirst<DK, DV, QBF16, SBF16, CONVV>)
+                       : reinterpret_cast<const void*>(&kda_decode_vfirst<DK, DV, QBF16, SBF16, CONVV>);
   return hipLaunchKernel(fn, dim3(static_cast<uint32_t>(nwg)), dim3(kWave), kargs, 0, stream);
 }
 
 using LaunchFn = hipError_t (*)(const DecodeArgs&, hipStream_t);
 
+template <int DK, int DV, bool QBF16, bool SBF16>
+LaunchFn pick_layout(int layout, bool conv_v) {
+  if (layout == KDA_STATE_V_FIRST)
+    return conv_v ? &launch_one<DK, DV, QBF16, SBF16, KDA_STATE_V_FIRST, true>
+                  : &launch_one<DK, DV, QBF16, SBF16, KDA_STATE_V_FIRST, false>;
+  return conv_v ? &launch_one<DK, DV, QBF16, SBF16, KDA_STATE_K_FIRST, true>
+                : &launch_one<DK, DV, QBF16, SBF16, KDA_STATE_K_FIRST, false>;
+}
+
 template <int DK, int DV>
-LaunchFn pick(bool qbf16, bool sbf16, int layout) {
-  const int key = (qbf16 ? 4 : 0) + (sbf16 ? 2 : 0) + (layout == KDA_STATE_V_FIRST ? 1 : 0);
-  switch (key) {
-    case 0: return &launch_one<DK, DV, false, false, KDA_STATE_K_FIRST>;
-    case 1: return &launch_one<DK, DV, false, false, KDA_STATE_V_FIRST>;
-    case 2: return &launch_one<DK, DV, false, true, KDA_STATE_K_FIRST>;
-    case 3: return &launch_one<DK, DV, false, true, KDA_STATE_V_FIRST>;
-    case 4: return &launch_one<DK, DV, true, false, KDA_STATE_K_FIRST>;
-    case 5: return &launch_one<DK, DV, true, false, KDA_STATE_V_FIRST>;
-    case 6: return &launch_one<DK, DV, true, true, KDA_STATE_K_FIRST>;
-    default: return &launch_one<DK, DV, true, true, KDA_STATE_V_FIRST>;
-  }
+LaunchFn pick(bool qbf16, bool sbf16, int layout, bool conv_v) {
+  if (qbf16) return sbf16 ? pick_layout<DK, DV, true, true>(layout, conv_v)
+                          : pick_layout<DK, DV, true, false>(layout, conv_v);
+  return sbf16 ? pick_layout<DK, DV, false, true>(layout, conv_v)
+               : pick_layout<DK, DV, false, false>(layout, conv_v);
 }
 
 template <int DK>
-LaunchFn pick_dv(int dv, bool qbf16, bool sbf16, int layout) {
+LaunchFn pick_dv(int dv, bool qbf16, bool sbf16, int layout, bool conv_v) {
   switch (dv) {
-    case 16: return pick<DK, 16>(qbf16, sbf16, layout);
-    case 32: return pick<DK, 32>(qbf16, sbf16, layout);
-    case 64: return pick<DK, 64>(qbf16, sbf16, layout);
-    case 128: return pick<DK, 128>(qbf16, sbf16, layout);
+    case 16: return pick<DK, 16>(qbf16, sbf16, layout, conv_v);
+    case 32: return pick<DK, 32>(qbf16, sbf16, layout, conv_v);
+    case 64: return pick<DK, 64>(qbf16, sbf16, layout, conv_v);
+    case 128: return pick<DK, 128>(qbf16, sbf16, layout, conv_v);
     default: return nullptr;
   }
+}
+
+template <int DK, bool XBF16>
+hipError_t launch_conv(const ConvQKArgs& args, hipStream_t stream) {
+  const int64_t nwg = static_cast<int64_t>(args.B) * args.H * 2;
+  void* kargs[] = {const_cast<ConvQKArgs*>(&args)};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&kda_conv_qk<DK, XBF16>),
+                         dim3(static_cast<uint32_t>(nwg)), dim3(kWave), kargs, 0, stream);
 }
 
 }  // namespace
 
 int launch_decode(const DecodeArgs& args, int dk, int dv, bool qkv_bf16, bool state_bf16,
-                  int state_layout, hipStream_t stream) {
+                  int state_layout, bool conv_v, hipStream_t stream) {
   LaunchFn fn = nullptr;
   switch (dk) {
-    case 16: fn = pick_dv<16>(dv, qkv_bf16, state_bf16, state_layout); break;
-    case 32: fn = pick_dv<32>(dv, qkv_bf16, state_bf16, state_layout); break;
-    case 64: fn = pick_dv<64>(dv, qkv_bf16, state_bf16, state_layout); break;
-    case 128: fn = pick_dv<128>(dv, qkv_bf16, state_bf16, state_layout); break;
+    case 16: fn = pick_dv<16>(dv, qkv_bf16, state_bf16, state_layout, conv_v); break;
+    case 32: fn = pick_dv<32>(dv, qkv_bf16, state_bf16, state_layout, conv_v); break;
+    case 64: fn = pick_dv<64>(dv, qkv_bf16, state_bf16, state_layout, conv_v); break;
+    case 128: fn = pick_dv<128>(dv, qkv_bf16, state_bf16, state_layout, conv_v); break;
+    default: break;
+  }
+  if (fn == nullptr) return KDA_ERR_UNSUPPORTED;
+  return fn(args, stream) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+int launch_conv_qk(const ConvQKArgs& args, int dk, bool x_bf16, hipStream_t stream) {
+  hipError_t (*fn)(const ConvQKArgs&, hipStream_t) = nullptr;
+  switch (dk) {
+    case 16: fn = x_bf16 ? &launch_conv<16, true> : &launch_conv<16, false>; break;
+    case 32: fn = x_bf16 ? &launch_conv<32, true> : &launch_conv<32, false>; break;
+    case 64: fn = x_bf16 ? &launch_conv<64, true> : &launch_conv<64, false>; break;
+    case 128: fn = x_bf16 ? &launch_conv<128, true> : &launch_conv<128, false>; break;
     default: break;
   }
   if (fn == nullptr) return KDA_ERR_UNSUPPORTED;

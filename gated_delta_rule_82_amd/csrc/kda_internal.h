@@ -24,13 +24,35 @@ struct DecodeArgs {
   int32_t B, T, H, HV, G, N;
   int32_t gate_mode;            // enum kda_gate_mode
   float lower_bound, l2_eps, scale;
+  // short convolution of the v stream (kda_decode_conv only; v is then the
+  // pre-convolution x_v)
+  const void* conv_w_v;         // [K, HV*dv] taps
+  float* conv_win_v;            // [N, K-1, HV*dv] windows
+  int32_t conv_k;               // K, 2..4
+  int32_t conv_w_bf16;          // taps stored as bf16
+};
+
+// Arguments of the q/k convolution kernel of kda_decode_conv.
+struct ConvQKArgs {
+  const void* x[2];             // pre-convolution q, k [T, H, dk]
+  const void* w[2];             // taps [K, H*dk]
+  float* win[2];                // windows [N, K-1, H*dk]
+  void* y[2];                   // convolved q, k [T, H, dk]
+  const int32_t* cu_seqlens;
+  const int32_t* state_indices;
+  int32_t B, T, H, N;
+  int32_t conv_k;
+  int32_t w_bf16;
 };
 
 // Enqueue the decode kernel for (dk, dv, q/k/v dtype, state dtype, state
 // layout) on `stream`.  Returns KDA_OK, KDA_ERR_UNSUPPORTED (no such
 // specialization) or KDA_ERR_LAUNCH.  Defined in kda_decode.hip.
 int launch_decode(const DecodeArgs& args, int dk, int dv, bool qkv_bf16, bool state_bf16,
-                  int state_layout, hipStream_t stream);
+                  int state_layout, bool conv_v, hipStream_t stream);
+
+// Enqueue the q/k convolution kernel.  Same return codes.
+int launch_conv_qk(const ConvQKArgs& args, int dk, bool x_bf16, hipStream_t stream);
 
 }  // namespace kda
 

@@ -36,12 +36,19 @@ KDA_STATE_K_FIRST = 0
 KDA_STATE_V_FIRST = 1
 STATE_LAYOUTS = {"k_first": KDA_STATE_K_FIRST, "v_first": KDA_STATE_V_FIRST}
 
-EXPORTED_SYMBOLS = ("kda_decode", "kda_check_host", "kda_status_string", "kda_abi_version")
+EXPORTED_SYMBOLS = ("kda_decode", "kda_decode_conv", "kda_check_host", "kda_status_string",
+                    "kda_abi_version")
+CONV_FIELDS = ("x_q", "x_k", "x_v", "w_q", "w_k", "w_v", "win_q", "win_k", "win_v", "q_conv",
+               "k_conv")
 
 
 class KdaTensor(ctypes.Structure):
     _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32),
                 ("ndim", ctypes.c_int32), ("shape", ctypes.c_int64 * 4)]
+
+
+class KdaConv(ctypes.Structure):
+    _fields_ = [(n, KdaTensor) for n in CONV_FIELDS]
 
 
 class KdaMode(ctypes.Structure):
@@ -80,6 +87,9 @@ def library() -> ctypes.CDLL:
     P = ctypes.POINTER(KdaTensor)
     lib.kda_decode.argtypes = [P] * 11 + [ctypes.POINTER(KdaMode), ctypes.c_void_p]
     lib.kda_decode.restype = ctypes.c_int
+    lib.kda_decode_conv.argtypes = [P, ctypes.POINTER(KdaConv)] + [P] * 7 + [ctypes.POINTER(KdaMode),
+                                                                        ctypes.c_void_p]
+    lib.kda_decode_conv.restype = ctypes.c_int
     lib.kda_check_host.argtypes = [ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
                                    ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
     lib.kda_check_host.restype = ctypes.c_int
@@ -122,6 +132,15 @@ def call_raw(tensors, mode: KdaMode, stream: int = 0) -> int:
     ptrs = [ctypes.byref(t) if t is not None else None for t in tensors]
     return lib.kda_decode(*ptrs, ctypes.byref(mode) if mode is not None else None,
                           ctypes.c_void_p(stream))
+
+
+def call_raw_conv(out, conv, rest, mode: KdaMode, stream: int = 0) -> int:
+    """Call kda_decode_conv on prepared descriptors: ``out``, a KdaConv (or
+    None), and the 7 remaining tensors (raw_gate .. state_indices)."""
+    lib = library()
+    ref = lambda t: ctypes.byref(t) if t is not None else None  # noqa: E731
+    return lib.kda_decode_conv(ref(out), ref(conv), *[ref(t) for t in rest], ref(mode),
+                               ctypes.c_void_p(stream))
 
 
 def _descriptor(t, name):
@@ -179,3 +198,35 @@ def check_host(cu_seqlens, state_indices, T: int, n_slots: int) -> int:
     P = ctypes.POINTER(ctypes.c_int32)
     return library().kda_check_host(cu.ctypes.data_as(P), idx.ctypes.data_as(P),
                                     len(idx), int(T), int(n_slots))
+
+
+CONV_REST = ("raw_gate", "beta_logits", "a_log", "dt_bias", "cu_seqlens", "state_pool",
+             "state_indices")
+
+
+def decode_conv(out, x_q, x_k, x_v, w_q, w_k, w_v, win_q, win_k, win_v, q_conv, k_conv, raw_gate,
+                beta_logits, a_log, dt_bias, cu_seqlens, state_pool, state_indices, *,
+                gate_mode="softplus", lower_bound=0.0, l2_eps=0.0, scale=0.0,
+                state_layout="k_first", stream: Optional[int] = None) -> None:
+    """The decode step with the short convolutions in front (see
+    kda_decode_conv in include/kda.h): x_q, x_k [1, T, H, dk] and x_v
+    [1, T, HV, dv] pre-convolution inputs; taps w_* [K, C]; windows win_*
+    [N, K-1, C] (updated in place); q_conv, k_conv [1, T, H, dk] receive the
+    convolved q and k (they may be x_q and x_k themselves)."""
+    import torch
+    conv_t = (x_q, x_k, x_v, w_q, w_k, w_v, win_q, win_k, win_v, q_conv, k_conv)
+    rest_t = (raw_gate, beta_logits, a_log, dt_bias, cu_seqlens, state_pool, state_indices)
+    conv = KdaConv(*[_descriptor(t, n) for t, n in zip(conv_t, CONV_FIELDS)])
+    rest = [_descriptor(t, n) for t, n in zip(rest_t, CONV_REST)]
+    out_d = _descriptor(out, "out")
+    dev = out.device
+    for t, n in zip(conv_t + rest_t, CONV_FIELDS + CONV_REST):
+        if t.device != dev:
+            raise ValueError(f"{n}: on {t.device}, expected {dev}")
+    mode = make_mode(gate_mode, lower_bound, l2_eps, scale, state_layout)
+    with torch.cuda.device(dev):
+        if stream is None:
+            stream = torch.cuda.current_stream(dev).cuda_stream
+        rc = call_raw_conv(out_d, conv, rest, mode, stream)
+    if rc != KDA_OK:
+        raise KdaError(rc, "kda_decode_conv")

@@ -262,3 +262,73 @@ def token_bytes(cfg: Workload, inp: Inputs) -> int:
     return (2 * T * cfg.H * cfg.DK * e + T * cfg.HV * cfg.DV * e + T * cfg.HV * cfg.DK * 4
             + T * cfg.HV * 4 + T * cfg.HV * cfg.DV * e + cfg.HV * 4 + cfg.HV * cfg.DK * 4
             + (cfg.B + 1) * 4 + cfg.B * 4)
+
+
+
+# ----------------------------------------------------------------------------
+# inputs of the decode step with the short convolutions in front
+# ----------------------------------------------------------------------------
+
+@dataclass
+class ConvInputs:
+    """Pre-convolution q/k/v (fp32 values, bf16-exact for bf16 workloads),
+    taps [K, C] and windows [N, K-1, C] for the three streams."""
+    K: int
+    x: dict            # "q", "k" [1, T, H, DK]; "v" [1, T, HV, DV]
+    w: dict            # "q", "k" [K, H*DK]; "v" [K, HV*DV]
+    win: dict          # "q", "k" [N, K-1, H*DK]; "v" [N, K-1, HV*DV]
+    taps_dtype: str = "f32"
+
+
+def draw_conv(inp: Inputs, K: int = 4, taps_dtype: str = "f32", seed_offset: int = 2) -> ConvInputs:
+    """Seeded conv inputs from their own generator (seed + seed_offset), so
+    the recurrence inputs of ``inp`` are unchanged.  Draw order: x_q, x_k,
+    x_v ~ N(0, 1); taps ~ N(0, 0.5) per stream; windows ~ N(0, 1).  Window
+    values hold earlier pre-convolution inputs, so they are bf16-exact when
+    the activations are bf16."""
+    cfg = inp.cfg
+    rng = np.random.default_rng(cfg.seed + seed_offset)
+    T = inp.T
+    shapes = {"q": (1, T, cfg.H, cfg.DK), "k": (1, T, cfg.H, cfg.DK), "v": (1, T, cfg.HV, cfg.DV)}
+    chans = {"q": cfg.H * cfg.DK, "k": cfg.H * cfg.DK, "v": cfg.HV * cfg.DV}
+
+    def act(a):
+        a = a.astype(np.float32)
+        return bf16_bits_to_f32(f32_to_bf16_bits(a)) if cfg.qkv_dtype == "bf16" else a
+
+    x = {s: act(rng.standard_normal(shapes[s], dtype=np.float32)) for s in "qkv"}
+    w = {}
+    for s in "qkv":
+        taps = (rng.standard_normal((K, chans[s]), dtype=np.float32) * np.float32(0.5)).astype(np.float32)
+        w[s] = bf16_bits_to_f32(f32_to_bf16_bits(taps)) if taps_dtype == "bf16" else taps
+    win = {s: act(rng.standard_normal((cfg.n_slots, K - 1, chans[s]), dtype=np.float32)) for s in "qkv"}
+    return ConvInputs(K, x, w, win, taps_dtype)
+
+
+def conv_to_device(ci: ConvInputs, qkv_dtype: str, device="cuda"):
+    """Device tensors keyed like the kda_decode_conv arguments, plus empty
+    fp32 q_conv / k_conv outputs."""
+    import torch
+    act = torch.bfloat16 if qkv_dtype == "bf16" else torch.float32
+    tap = torch.bfloat16 if ci.taps_dtype == "bf16" else torch.float32
+    d = {}
+    for s in "qkv":
+        d["x_" + s] = torch.from_numpy(ci.x[s]).to(device).to(act)
+        d["w_" + s] = torch.from_numpy(ci.w[s]).to(device).to(tap)
+        d["win_" + s] = torch.from_numpy(ci.win[s]).to(device)
+    d["q_conv"] = torch.empty(d["x_q"].shape, dtype=torch.float32, device=device)
+    d["k_conv"] = torch.empty(d["x_k"].shape, dtype=torch.float32, device=device)
+    return d
+
+
+def conv_bytes(cfg: Workload, inp: Inputs, K: int) -> int:
+    """Algorithmic bytes the convolutions add to a step: the pre-convolution
+    inputs, the fp32 convolved q/k written and read back, the taps, and the
+    fp32 windows of every active request read and written."""
+    e = 2 if cfg.qkv_dtype == "bf16" else 4
+    T = inp.T
+    cqk, cv = cfg.H * cfg.DK, cfg.HV * cfg.DV
+    counts = np.diff(inp.cu_seqlens)
+    active = int(np.sum((counts > 0) & (inp.state_indices >= 0)))
+    return (T * (2 * cqk + cv) * e + 2 * (T * 2 * cqk * 4) + K * (2 * cqk + cv) * 4
+            + 2 * active * (K - 1) * (2 * cqk + cv) * 4)

@@ -54,7 +54,7 @@ extern "C" {
 /* hipStream_t, declared here so that this header needs no HIP include. */
 typedef struct ihipStream_t* hipStream_t;
 
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 
 /* Status codes.  Zero is success; errors are negative. */
 enum kda_status {
@@ -150,6 +150,53 @@ int kda_decode(const kda_tensor* out, const kda_tensor* q, const kda_tensor* k,
                const kda_tensor* dt_bias, const kda_tensor* cu_seqlens,
                const kda_tensor* state_pool, const kda_tensor* state_indices,
                const kda_mode* mode, hipStream_t stream);
+
+/*
+ * The short causal convolutions in front of the recurrence ("KDA Block TKG
+ * Kernel API Reference": parameters conv_w and conv_state, and the
+ * Background's short convolutions with SiLU; K = 4 for Kimi K3).  For each
+ * stream (q, k, v) and channel c, per token t of a request:
+ *     y_t[c] = SiLU(sum_{j<K} w[j][c] * x_{t-K+1+j}[c])
+ * where the K-1 inputs before the request's first token come from the
+ * stream's window, tap 0 meets the oldest position, and after the request's
+ * last token the window holds its last K-1 pre-convolution inputs.  The
+ * convolved streams enter the recurrence in fp32, unrounded (the block
+ * keeps intermediates on chip, "KDA Block TKG" Background); only the output
+ * is rounded to its dtype.  Channels are head-outer (h*dk + d), matching the
+ * q/k/v tensors.
+ */
+typedef struct kda_conv {
+  kda_tensor x_q;     /* [1, T, H, dk]  pre-convolution q; bf16 or f32        */
+  kda_tensor x_k;     /* [1, T, H, dk]  pre-convolution k; dtype of x_q       */
+  kda_tensor x_v;     /* [1, T, HV, dv] pre-convolution v; dtype of x_q       */
+  kda_tensor w_q;     /* [K, H*dk]  taps, 2 <= K <= 4; f32 or bf16            */
+  kda_tensor w_k;     /* [K, H*dk]  dtype of w_q                              */
+  kda_tensor w_v;     /* [K, HV*dv] dtype of w_q                              */
+  kda_tensor win_q;   /* [N, K-1, H*dk]  f32 windows, oldest first, IN/OUT    */
+  kda_tensor win_k;   /* [N, K-1, H*dk]  slot state_indices[b], like the pool */
+  kda_tensor win_v;   /* [N, K-1, HV*dv]                                      */
+  kda_tensor q_conv;  /* [1, T, H, dk] OUT: convolved q, f32; may be x_q     */
+                      /*   itself when x_q is f32 (convolved in place)        */
+  kda_tensor k_conv;  /* [1, T, H, dk] OUT: convolved k, f32; may be x_k      */
+} kda_conv;
+
+/*
+ * kda_decode_conv - the decode step with the short convolutions in front:
+ * convolve q, k and v of every request (windows updated in place) and
+ * advance the recurrence on the result, as kda_decode does with
+ * q = q_conv, k = k_conv and v = the convolved x_v.  Two kernels are
+ * enqueued on `stream`: one convolves q and k per (request, key head,
+ * channel); the recurrence kernel convolves v itself, each v channel
+ * belonging to exactly one wave.  A skipped request (negative index) gets
+ * zero rows in out, q_conv and k_conv and keeps its windows; an empty
+ * request changes nothing.  Arguments other than `conv` are those of
+ * kda_decode; every check runs before any device work.
+ */
+int kda_decode_conv(const kda_tensor* out, const kda_conv* conv, const kda_tensor* raw_gate,
+                    const kda_tensor* beta_logits, const kda_tensor* a_log,
+                    const kda_tensor* dt_bias, const kda_tensor* cu_seqlens,
+                    const kda_tensor* state_pool, const kda_tensor* state_indices,
+                    const kda_mode* mode, hipStream_t stream);
 
 /*
  * kda_check_host - validate host copies of the decode metadata.

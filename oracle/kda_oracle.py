@@ -42,9 +42,9 @@ the design notes of the repository):
     request's tokens, and rounded to nearest-even when stored.
   * short convolution: y_t = SiLU(sum_j w[j] * x_{t-K+1+j}) per channel with
     no bias; windows are slotted like the state ([N, K-1, C], oldest first,
-    channels head-outer as in the q/k/v tensors); the convolved q, k, v are
-    handed to the recurrence in the activation dtype (the model's conv layer
-    returns them in it), i.e. rounded to nearest-even for bf16 inputs.
+    channels head-outer as in the q/k/v tensors).  In the fused step the
+    convolved q, k, v go to the recurrence unrounded ([TKG] Background: the
+    block keeps every intermediate on chip), so only the output is rounded.
 
 Parity status: every function below is pinned by the CPU tests
 (``tests/test_oracle_pins.py``) against closed forms, hand-worked values,
@@ -336,16 +336,16 @@ def short_conv(x, window, w):
 
 
 def kda_decode_conv(x_q, x_k, x_v, w_q, w_k, w_v, win_q, win_k, win_v, raw_gate,
-                    beta_logits, a_log, dt_bias, cu_seqlens, state_pool, state_indices, *,
-                    act_dtype="bf16", **decode_kw):
+                    beta_logits, a_log, dt_bias, cu_seqlens, state_pool, state_indices,
+                    **decode_kw):
     """The decode step with the short convolutions in front of the recurrence.
 
     x_q, x_k [1, T, H, dk] and x_v [1, T, HV, dv] are the pre-convolution
     projections; w_* [K, C] the taps with C = H*dk (q, k) or HV*dv (v),
     channels head-outer; win_* [N, K-1, C] the slotted windows (slot
     state_indices[b], like the recurrent state).  Per request, each stream
-    is convolved over its tokens (short_conv), rounded to the activation
-    dtype, and the recurrence (kda_decode) runs on the result.  A skipped
+    is convolved over its tokens (short_conv) and the recurrence (kda_decode)
+    runs on the unrounded result.  A skipped
     request (negative index) leaves its windows alone and gets zero q/k
     rows; an empty request changes nothing.
 
@@ -366,8 +366,6 @@ def kda_decode_conv(x_q, x_k, x_v, w_q, w_k, w_v, win_q, win_k, win_v, raw_gate,
         for s in range(3):
             flat = x[s][t0:t1].reshape(t1 - t0, -1)
             y, new_win = short_conv(flat, win[s][slot], w[s])
-            if act_dtype == "bf16":
-                y = round_to_bf16(y)
             conv[s][t0:t1] = y.reshape(x[s][t0:t1].shape)
             win[s][slot] = new_win
     out, pool = kda_decode(conv[0][None], conv[1][None], conv[2][None], raw_gate, beta_logits,

@@ -181,3 +181,64 @@ def parity_case(inp, device="cuda", sample=None, check_untouched=True, mode_over
         del before
     stats["tiles"] = len(tiles)
     return stats, out_t, pool_t
+
+
+CONV_REL = 1e-5   # convolved q/k (fp32 SiLU of a K-term sum) against the oracle
+
+
+def conv_parity_case(inp, ci, device="cuda", sample=None, in_place=False):
+    """kda_decode_conv on the GPU against the oracle's decode step with the
+    convolutions in front.  Checks outputs and states as parity_case does,
+    the convolved q/k (relative CONV_REL), and every window bit-exact (they
+    hold copies of pre-convolution inputs)."""
+    import torch
+    from gated_delta_rule_82_amd import kda
+    cfg = inp.cfg
+    dev = wl.to_device(inp, device)
+    cd = wl.conv_to_device(ci, cfg.qkv_dtype, device)
+    if in_place:          # fp32 activations convolved in place
+        cd["q_conv"], cd["k_conv"] = cd["x_q"], cd["x_k"]
+    pool_t = wl.device_pool(inp, device)
+    tiles = choose_tiles(inp, sample)
+    valid = [(b, hv) for b, hv in tiles if inp.state_indices[b] >= 0]
+    slots = [int(inp.state_indices[b]) for b, hv in valid]
+    hvs = [hv for b, hv in valid]
+    init = gather_tiles(pool_t, slots, hvs) if valid else []
+    out_t = wl.empty_out(inp, device)
+    out_t.fill_(float("nan"))
+    if not in_place:
+        cd["q_conv"].fill_(float("nan"))
+        cd["k_conv"].fill_(float("nan"))
+    kda.decode_conv(out_t, cd["x_q"], cd["x_k"], cd["x_v"], cd["w_q"], cd["w_k"], cd["w_v"],
+                    cd["win_q"], cd["win_k"], cd["win_v"], cd["q_conv"], cd["k_conv"],
+                    dev["raw_gate"], dev["beta_logits"], dev["a_log"], dev["dt_bias"],
+                    dev["cu_seqlens"], pool_t, dev["state_indices"], gate_mode=cfg.gate_mode,
+                    lower_bound=cfg.lower_bound, state_layout=cfg.state_layout)
+    torch.cuda.synchronize()
+    out_gpu = out_to_f64(out_t)
+    after = gather_tiles(pool_t, slots, hvs) if valid else []
+
+    pool = {(s, hv): S for s, hv, S in zip(slots, hvs, init)}
+    lb = cfg.lower_bound if cfg.gate_mode == ko.GATE_LOWER_BOUND else None
+    out_ref, pool_ref, wq, wk, wv, qc, kc = ko.kda_decode_conv(
+        ci.x["q"], ci.x["k"], ci.x["v"], ci.w["q"], ci.w["k"], ci.w["v"], ci.win["q"],
+        ci.win["k"], ci.win["v"], inp.raw_gate, inp.beta_logits, inp.a_log, inp.dt_bias,
+        inp.cu_seqlens, pool, inp.state_indices, tiles=tiles, gate_mode=cfg.gate_mode,
+        lower_bound=lb, state_layout=cfg.state_layout, state_dtype=cfg.state_dtype)
+    stats = compare_outputs(inp, tiles, out_gpu, out_ref)
+    if valid:
+        stats.update(compare_states(after, [pool_ref[(s, hv)] for s, hv in zip(slots, hvs)],
+                                    cfg.state_dtype))
+    for name, ref in (("win_q", wq), ("win_k", wk), ("win_v", wv)):
+        got = cd[name].cpu().numpy().astype(np.float64)
+        assert np.array_equal(got, ref), f"{name} differs"
+    worst = 0.0
+    for name, ref in (("q_conv", qc), ("k_conv", kc)):
+        got = cd[name].float().cpu().numpy().astype(np.float64)
+        assert np.isfinite(got).all(), f"{name} has non-finite values"
+        bound = CONV_REL * np.abs(ref) + 1e-6 * max(float(np.abs(ref).max()), 1e-30)
+        worst = max(worst, float(np.max(np.abs(got - ref) / bound)))
+    assert worst <= 1.0, f"convolved q/k exceed tolerance (ratio {worst:.3f})"
+    stats["conv_ratio"] = worst
+    stats["tiles"] = len(tiles)
+    return stats

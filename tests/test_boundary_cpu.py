@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = kda.library()
-    assert lib.kda_abi_version() == 2
+    assert lib.kda_abi_version() == 3
     codes = [kda.KDA_OK, kda.KDA_ERR_NULL, kda.KDA_ERR_DTYPE, kda.KDA_ERR_SHAPE,
              kda.KDA_ERR_UNSUPPORTED, kda.KDA_ERR_MODE, kda.KDA_ERR_LAUNCH,
              kda.KDA_ERR_PRECONDITION]
@@ -210,3 +210,68 @@ def test_state_layout_and_dtype_checks():
     d = descriptors()
     d["state_pool"] = kda.raw_tensor(d["state_pool"].data, kda.KDA_BF16, (8, 4, 128, 128))
     assert call(d, gate_mode=9) == kda.KDA_ERR_MODE
+
+
+
+# ---------------------------------------------------------------------------
+# kda_decode_conv argument checking (never reaches a launch)
+# ---------------------------------------------------------------------------
+
+_FAKE_CONV = [0x4000000 + 0x100000 * i for i in range(11)]
+
+
+def conv_descriptors(B=2, T=3, H=2, HV=4, DK=128, DV=128, N=8, K=4, act=kda.KDA_BF16,
+                     taps=kda.KDA_F32):
+    d = descriptors(B=B, T=T, H=H, HV=HV, DK=DK, DV=DV, N=N, qkv=act)
+    shapes = {
+        "x_q": (act, (1, T, H, DK)), "x_k": (act, (1, T, H, DK)), "x_v": (act, (1, T, HV, DV)),
+        "w_q": (taps, (K, H * DK)), "w_k": (taps, (K, H * DK)), "w_v": (taps, (K, HV * DV)),
+        "win_q": (kda.KDA_F32, (N, K - 1, H * DK)), "win_k": (kda.KDA_F32, (N, K - 1, H * DK)),
+        "win_v": (kda.KDA_F32, (N, K - 1, HV * DV)),
+        "q_conv": (kda.KDA_F32, (1, T, H, DK)), "k_conv": (kda.KDA_F32, (1, T, H, DK)),
+    }
+    conv = {n: kda.raw_tensor(_FAKE_CONV[i], *shapes[n]) for i, n in enumerate(kda.CONV_FIELDS)}
+    return d, conv
+
+
+def call_conv(d, conv, **mode_kw):
+    c = None if conv is None else kda.KdaConv(*[conv[n] for n in kda.CONV_FIELDS])
+    return kda.call_raw_conv(d["out"], c, [d[n] for n in kda.CONV_REST], kda.make_mode(**mode_kw), 0)
+
+
+def test_conv_nothing_to_do_and_null():
+    d, conv = conv_descriptors(B=0, T=0)
+    assert call_conv(d, conv) == kda.KDA_OK
+    assert call_conv(d, None) == kda.KDA_ERR_NULL
+    d, conv = conv_descriptors()
+    conv["win_k"] = kda.raw_tensor(0, kda.KDA_F32, (8, 3, 256))
+    assert call_conv(d, conv) == kda.KDA_ERR_NULL
+
+
+@pytest.mark.parametrize("K", [1, 5, 8])
+def test_conv_width_outside_2_to_4_is_unsupported(K):
+    d, conv = conv_descriptors(K=K)
+    assert call_conv(d, conv) == kda.KDA_ERR_UNSUPPORTED
+
+
+def test_conv_dtype_and_shape_errors():
+    d, conv = conv_descriptors()
+    conv["x_q"] = kda.raw_tensor(conv["x_q"].data, kda.KDA_F32, (1, 3, 2, 128))
+    assert call_conv(d, conv) == kda.KDA_ERR_DTYPE
+    d, conv = conv_descriptors()
+    conv["w_v"] = kda.raw_tensor(conv["w_v"].data, kda.KDA_BF16, (4, 512))
+    assert call_conv(d, conv) == kda.KDA_ERR_DTYPE
+    d, conv = conv_descriptors()
+    conv["win_q"] = kda.raw_tensor(conv["win_q"].data, kda.KDA_BF16, (8, 3, 256))
+    assert call_conv(d, conv) == kda.KDA_ERR_DTYPE
+    d, conv = conv_descriptors()      # the convolved q/k are fp32
+    conv["k_conv"] = kda.raw_tensor(conv["k_conv"].data, kda.KDA_BF16, (1, 3, 2, 128))
+    assert call_conv(d, conv) == kda.KDA_ERR_DTYPE
+    for name, shape in (("win_v", (8, 3, 256)), ("win_q", (8, 2, 256)), ("w_k", (4, 512)),
+                        ("w_k", (3, 256)), ("x_k", (1, 3, 2, 64)), ("q_conv", (1, 3, 4, 128))):
+        d, conv = conv_descriptors()
+        conv[name] = kda.raw_tensor(conv[name].data, conv[name].dtype, shape)
+        assert call_conv(d, conv) == kda.KDA_ERR_SHAPE, name
+    # the recurrence arguments are checked as in kda_decode
+    d, conv = conv_descriptors()
+    assert call_conv(d, conv, gate_mode="lower_bound", lower_bound=1.0) == kda.KDA_ERR_MODE
