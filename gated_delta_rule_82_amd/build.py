@@ -2,9 +2,9 @@
 
     python -m gated_delta_rule_82_amd.build
 
-The host argument checker is plain C++ (g++); the kernel file goes through
-hipcc for gfx950 with packed-fp32 instructions disabled; hipcc links both
-into ``gated_delta_rule_82_amd/lib/libkda.so``.
+The host argument checker is plain C++ (g++); the kernel files (decode and
+chunked prefill) go through hipcc for gfx950 with packed-fp32 instructions
+disabled; hipcc links them into ``gated_delta_rule_82_amd/lib/libkda.so``.
 """
 from __future__ import annotations
 
@@ -49,18 +49,40 @@ def _run(cmd, verbose):
         print(out, flush=True)
 
 
+def _run_all(cmds, verbose):
+    if verbose:
+        for cmd in cmds:
+            print("+", " ".join(cmd), flush=True)
+    procs = [subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+             for cmd in cmds]
+    failed = []
+    for cmd, proc in zip(cmds, procs):
+        out, _ = proc.communicate()
+        out = "\n".join(line for line in out.splitlines()
+                        if "packed-fp32-ops' is not a recognized feature" not in line)
+        if proc.returncode != 0:
+            failed.append(f"command failed ({proc.returncode}): {' '.join(cmd)}\n{out}")
+        elif verbose and out.strip():
+            print(out, flush=True)
+    if failed:
+        raise RuntimeError("\n".join(failed))
+
+
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
     os.makedirs(LIBDIR, exist_ok=True)
     hipcc = _hipcc()
     api_o = os.path.join(BUILD, "kda_api.o")
-    dec_o = os.path.join(BUILD, "kda_decode.o")
+    kernels = ("kda_decode", "kda_prefill")
+    objs = [os.path.join(BUILD, f"{name}.o") for name in kernels]
     _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", f"-I{INCLUDE}", f"-I{CSRC}",
           "-c", os.path.join(CSRC, "kda_api.cpp"), "-o", api_o], verbose)
-    _run([hipcc, *HIP_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", "-c",
-          os.path.join(CSRC, "kda_decode.hip"), "-o", dec_o], verbose)
+    # the kernel files compile in parallel (each takes tens of seconds)
+    cmds = [[hipcc, *HIP_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", "-c",
+             os.path.join(CSRC, f"{name}.hip"), "-o", obj] for name, obj in zip(kernels, objs)]
+    _run_all(cmds, verbose)
     tmp = LIB + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", api_o, dec_o, "-o", tmp,
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", api_o, *objs, "-o", tmp,
           "-Wl,-z,defs", "-Wl,--no-undefined",
           f"-Wl,--version-script={os.path.join(CSRC, 'libkda.map')}"], verbose)
     os.replace(tmp, LIB)

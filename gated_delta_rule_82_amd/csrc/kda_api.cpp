@@ -299,4 +299,20 @@ int kda_decode_conv(const kda_tensor* out, const kda_conv* conv, const kda_tenso
                             true, stream);
 }
 
+int kda_prefill(const kda_tensor* out, const kda_tensor* q, const kda_tensor* k,
+                const kda_tensor* v, const kda_tensor* raw_gate,
+                const kda_tensor* beta_logits, const kda_tensor* a_log,
+                const kda_tensor* dt_bias, const kda_tensor* cu_seqlens,
+                const kda_tensor* state_pool, const kda_tensor* state_indices,
+                const kda_mode* mode, int32_t matmul, hipStream_t stream) {
+  Plan plan;
+  KDA_TRY(plan_decode(out, q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens,
+                      state_pool, state_indices, mode, &plan));
+  if (matmul != KDA_MATMUL_SPLIT_BF16 && matmul != KDA_MATMUL_F32) return KDA_ERR_MODE;
+  if (plan.dk < 32 || plan.dv < 32) return KDA_ERR_UNSUPPORTED;
+  if (plan.empty) return KDA_OK;
+  return kda::launch_prefill(plan.args, plan.dk, plan.dv, plan.qkv_bf16, plan.state_bf16,
+                             plan.layout, matmul, stream);
+}
+
 }  // extern "C"

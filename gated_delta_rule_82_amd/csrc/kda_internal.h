@@ -51,6 +51,11 @@ struct ConvQKArgs {
 int launch_decode(const DecodeArgs& args, int dk, int dv, bool qkv_bf16, bool state_bf16,
                   int state_layout, bool conv_v, hipStream_t stream);
 
+// Enqueue the chunked prefill kernel (dk, dv in {32, 64, 128}; matmul an
+// enum kda_matmul).  Same return codes.  Defined in kda_prefill.hip.
+int launch_prefill(const DecodeArgs& args, int dk, int dv, bool qkv_bf16, bool state_bf16,
+                   int state_layout, int matmul, hipStream_t stream);
+
 // Enqueue the q/k convolution kernel.  Same return codes.
 int launch_conv_qk(const ConvQKArgs& args, int dk, bool x_bf16, hipStream_t stream);
 

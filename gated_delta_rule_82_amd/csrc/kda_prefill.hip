@@ -1,0 +1,785 @@
+// kda_prefill.hip - the KDA recurrence over whole requests (prefill), chunk
+// by chunk on the CDNA4 matrix cores (gfx950).
+//
+// Operation: the same per-token recurrence as kda_decode ("Delta-rule
+// write" page, naive_recurrent_kda code excerpt; "KdaDecode" tensor
+// contract; "KDA Block TKG" l2_eps / scale / lower_bound).  The model runs
+// this step as chunk_kda for a whole sequence ("Delta-rule write" page,
+// modeling_kimi_linear.py excerpt); the pages do not pin that kernel's
+// internals, so what is fixed is the token-by-token result.
+//
+// Chunk form.  Take C = 16 tokens at a time.  With Gamma_t[d] the running
+// sum of the log-decays g since the chunk start (inclusive of token t),
+// S0 the state before the chunk and kh, qh the normalised keys and scaled
+// queries:
+//   X  = V - Kt S0            Kt[t]  = kh_t * exp(Gamma_t)
+//   Y  = Qt S0                Qt[t]  = qh_t * exp(Gamma_t)
+//   (I + L) U = X             L[t,s] = beta_s P[t,s]          (s < t)
+//   O  = Y + R' U             R'[t,s] = beta_s R[t,s]         (s <= t)
+//   S  = diag(exp(Gamma_last)) S0 + Kup^T U,
+//                             Kup[s] = beta_s kh_s exp(Gamma_last - Gamma_s)
+//   P[t,s] = sum_d kh_t[d] kh_s[d] exp(Gamma_t[d] - Gamma_s[d]), R the same
+//   with qh_t.  U holds the per-token corrections v_t - kh_t^T(decayed S);
+// unrolling the recurrence over the chunk gives exactly these equations, so
+// the result differs from the token loop only in rounding order.  The L2
+// norms are per-token scale factors, so every product above runs on the raw
+// q, k and the norms are applied to its rows or columns afterwards:
+//   X = V - diag(rk) (Kt_raw S0),  O = diag(rq) (Qt_raw S0 + R_raw U'),
+//   S = diag(exp(Gamma_last)) S0 + Kup_raw^T U',  U' = diag(beta rk) U,
+//   L = diag(rk) P_raw diag(rk beta).
+// A ragged last chunk is padded with tokens whose q, k, v, beta and g are
+// zero; they change nothing.
+//
+// P_raw and R_raw are sums over the key channels, so each wave adds up the
+// part of its own channels.  For a channel set whose decay span
+// max(-Gamma_last[d]) is at most kSafeSpan, that part is one matrix product
+// of Kp = k exp(Gamma - c) and Ks = k exp(c - Gamma) with c = Gamma_last / 2:
+// every factor then lies within exp(+-kSafeSpan / 2), far from fp32 overflow
+// and from subnormals.  A wider span (a strong softplus gate) takes the
+// pair-by-pair sums, with exp(Gamma_t - Gamma_s) <= 1 formed per term.
+//
+// Work decomposition.  A workgroup owns one (request, value head) tile and
+// walks the request's chunks in order; wave w owns value columns
+// [32w, 32w + 32), and its state slab S[:, 32w:32w+32] stays in the wave's
+// MFMA accumulators for the whole request.  An accumulator tile holds rows
+// 4*(lane/16) + i (i = 0..3) of column lane % 16; an A (B) operand holds,
+// per lane, row (column) lane % 16 and a set of reduction indices chosen by
+// lane / 16.  The reduction order inside a product is free, so each product
+// is oriented to take its operands where they already are:
+//   * acc(M) is the B operand of M and the A operand of M^T.  X = Kt_raw S
+//     and Y^T = S^T Qt_raw^T both read the state straight from its
+//     accumulators; U = T X reads X, O^T = Y^T + U'^T R_raw^T and the state
+//     update Kup_raw^T U' read U'.  O comes out transposed, so each lane
+//     stores four consecutive values of one output row.
+//   * The per-chunk elementwise work runs in the operand layout itself: lane
+//     (token lane % 16, quarter lane / 16) handles 8 consecutive channels of
+//     its token.  P and R partials are then one product of registers (A and
+//     B from the same lanes), the decay prefix over tokens is a DPP scan
+//     within each 16-lane row, and V enters X through a product with an
+//     identity B operand instead of a gather.
+// Per chunk: every wave builds its channels' operands and partials and
+// publishes them in LDS (Kt, Qt, Kup^T, exp(Gamma_last), norms, P and R
+// partials); after one workgroup barrier each wave assembles L, solves
+// T = (I + L)^-1 itself (right-looking substitution, 16 lanes) and runs X,
+// Y^T, U, O^T and the state update on its slab; a second barrier frees the
+// tables for the next chunk.  The next chunk's inputs are loaded into
+// registers while the current one is processed, and the barriers fence LDS
+// only, so those loads stay in flight.  The state makes one trip from HBM
+// and one back per request.
+//
+// Matrix precision.  KDA_MATMUL_F32 uses the fp32 matrix instruction
+// (v_mfma_f32_16x16x4_f32): fp32 products, fp32 sums.  KDA_MATMUL_SPLIT_BF16
+// writes each fp32 operand as hi + lo, both bf16 (round to nearest even),
+// and sums the three products hi*hi + hi*lo + lo*hi on the bf16 matrix
+// instructions (16x16x32 and 16x16x16): each operand keeps 16 significant
+// bits and the dropped lo*lo term is below 2^-16 of the product, at a third
+// of the fp32 instruction's cost per product.  (This is the classic
+// split-precision product, e.g. Henry, Tang and Heinecke, "Leveraging the
+// bfloat16 artificial intelligence datatype for higher-precision
+// computations", ARITH 2019.)
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kda.h"
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+constexpr int kChunk = 16;          // tokens per chunk: one MFMA M / K tile
+constexpr float kSafeSpan = 80.0f;  // largest decay span of the one-product P, R
+constexpr int kPT = kChunk + 4;     // pitch of the 16-column LDS tables
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// Barrier for LDS traffic only: outstanding global loads (the next chunk's
+// inputs) and stores (outputs) are not waited for.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Orders this wave's own LDS writes before its later LDS reads of other
+// lanes' data (the hardware keeps a wave's LDS operations in order; this
+// keeps the compiler from moving them).
+__device__ __forceinline__ void wave_lds_order() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront", "local");
+}
+
+// ---------------------------------------------------------------------------
+// operand fragments and the two matrix precisions
+// ---------------------------------------------------------------------------
+
+// N fp32 operand values of one lane: the reduction indices (lane / 16, j)
+// of a 16x16xK product, K = 4N (N = 8: K = 32; N = 4: K = 16).
+template <int PREC, int N>
+struct Frag;
+
+template <int N>
+struct Frag<KDA_MATMUL_F32, N> {
+  float v[N];
+};
+
+template <int N>
+struct Frag<KDA_MATMUL_SPLIT_BF16, N> {
+  typedef __bf16 vec __attribute__((ext_vector_type(N)));
+  vec hi, lo;
+};
+
+template <int PREC, int N>
+__device__ __forceinline__ Frag<PREC, N> make_frag(const float (&x)[N]) {
+  Frag<PREC, N> f;
+  if constexpr (PREC == KDA_MATMUL_F32) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) f.v[j] = x[j];
+  } else {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const __bf16 h = static_cast<__bf16>(x[j]);
+      f.hi[j] = h;
+      f.lo[j] = static_cast<__bf16>(x[j] - static_cast<float>(h));
+    }
+  }
+  return f;
+}
+
+// acc += A B over the fragment's K indices.
+template <int PREC, int N>
+__device__ __forceinline__ void mma(f32x4& acc, const Frag<PREC, N>& a, const Frag<PREC, N>& b) {
+  if constexpr (PREC == KDA_MATMUL_F32) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[j], b.v[j], acc, 0, 0, 0);
+  } else if constexpr (N == 8) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.hi, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.lo, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, acc, 0, 0, 0);
+  } else {
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.lo, b.hi, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.hi, b.lo, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.hi, b.hi, acc, 0, 0, 0);
+  }
+}
+
+// acc += A I_nt where I_nt is the identity restricted to value tile nt: the
+// K = 32 indices (g, j) stand for the slab's columns 8g + j, B[(g, j)][n] =
+// [8g + j == 16 nt + n].  A bf16 value is exact in the hi part alone.
+template <int PREC, bool EXACT_BF16>
+__device__ __forceinline__ void mma_identity(f32x4& acc, const float (&a)[8], int nt, int n, int g) {
+  float e[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) e[j] = 8 * g + j == 16 * nt + n ? 1.0f : 0.0f;
+  if constexpr (PREC == KDA_MATMUL_F32) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], e[j], acc, 0, 0, 0);
+  } else {
+    const Frag<PREC, 8> fa = make_frag<PREC, 8>(a);
+    const Frag<PREC, 8> fe = make_frag<PREC, 8>(e);
+    if constexpr (!EXACT_BF16) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa.lo, fe.hi, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa.hi, fe.hi, acc, 0, 0, 0);
+  }
+}
+
+template <int PREC>
+__device__ __forceinline__ Frag<PREC, 8> acc_frag8(const f32x4& lo, const f32x4& hi) {
+  const float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return make_frag<PREC, 8>(v);
+}
+
+template <int PREC>
+__device__ __forceinline__ Frag<PREC, 4> acc_frag4(const f32x4& x) {
+  const float v[4] = {x[0], x[1], x[2], x[3]};
+  return make_frag<PREC, 4>(v);
+}
+
+// [16][DK] operand rows in LDS (Kt_raw, Qt_raw), stored already in the form
+// the matrix instruction takes: fp32, or the bf16 hi and lo parts.  Rows
+// are written 8 channels at a time and read as K = 32 slices in the order of
+// two stacked accumulator tiles: value j of lane group g is channel
+// 32s + 16 (j / 4) + 4g + j % 4.
+template <int PREC, int DK>
+struct RowTable;
+
+template <int DK>
+struct RowTable<KDA_MATMUL_F32, DK> {
+  static constexpr int P = DK + 4;
+  float v[kChunk][P];
+  __device__ __forceinline__ void store8(int t, int d0, const float (&x)[8]) {
+    *reinterpret_cast<f32x4*>(&v[t][d0]) = f32x4{x[0], x[1], x[2], x[3]};
+    *reinterpret_cast<f32x4*>(&v[t][d0 + 4]) = f32x4{x[4], x[5], x[6], x[7]};
+  }
+  __device__ __forceinline__ Frag<KDA_MATMUL_F32, 8> frag8(int row, int s, int g) const {
+    const f32x4 x0 = *reinterpret_cast<const f32x4*>(&v[row][32 * s + 4 * g]);
+    const f32x4 x1 = *reinterpret_cast<const f32x4*>(&v[row][32 * s + 16 + 4 * g]);
+    Frag<KDA_MATMUL_F32, 8> f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f.v[j] = x0[j];
+      f.v[4 + j] = x1[j];
+    }
+    return f;
+  }
+};
+
+template <int DK>
+struct RowTable<KDA_MATMUL_SPLIT_BF16, DK> {
+  static constexpr int P = DK + 8;
+  __bf16 hi[kChunk][P];
+  __bf16 lo[kChunk][P];
+  __device__ __forceinline__ void store8(int t, int d0, const float (&x)[8]) {
+    const Frag<KDA_MATMUL_SPLIT_BF16, 8> f = make_frag<KDA_MATMUL_SPLIT_BF16, 8>(x);
+    *reinterpret_cast<bf16x8*>(&hi[t][d0]) = f.hi;
+    *reinterpret_cast<bf16x8*>(&lo[t][d0]) = f.lo;
+  }
+  __device__ __forceinline__ Frag<KDA_MATMUL_SPLIT_BF16, 8> frag8(int row, int s, int g) const {
+    const bf16x4 h0 = *reinterpret_cast<const bf16x4*>(&hi[row][32 * s + 4 * g]);
+    const bf16x4 h1 = *reinterpret_cast<const bf16x4*>(&hi[row][32 * s + 16 + 4 * g]);
+    const bf16x4 l0 = *reinterpret_cast<const bf16x4*>(&lo[row][32 * s + 4 * g]);
+    const bf16x4 l1 = *reinterpret_cast<const bf16x4*>(&lo[row][32 * s + 16 + 4 * g]);
+    Frag<KDA_MATMUL_SPLIT_BF16, 8> f;
+    f.hi = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+    f.lo = __builtin_shufflevector(l0, l1, 0, 1, 2, 3, 4, 5, 6, 7);
+    return f;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// memory helpers
+// ---------------------------------------------------------------------------
+
+template <bool BF16>
+__device__ __forceinline__ float load_elem(const void* base, int64_t off) {
+  if constexpr (BF16) return bf16_to_f32(static_cast<const uint16_t*>(base)[off]);
+  else return static_cast<const float*>(base)[off];
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store_elem(void* base, int64_t off, float x) {
+  if constexpr (BF16) static_cast<uint16_t*>(base)[off] = static_cast<uint16_t>(f32_to_bf16_rne(x));
+  else static_cast<float*>(base)[off] = x;
+}
+
+// 8 consecutive elements at a 16-byte aligned element offset, kept in their
+// storage form (bf16 pairs or fp32).
+template <bool BF16>
+struct Run8 {
+  static constexpr int W = BF16 ? 4 : 8;
+  uint32_t w[W];
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < W; ++i) w[i] = 0;
+  }
+  __device__ __forceinline__ void load(const void* base, int64_t off) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const char*>(base) + off * (BF16 ? 2 : 4));
+#pragma unroll
+    for (int i = 0; i < W / 4; ++i) {
+      const u32x4 x = p[i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[4 * i + j] = x[j];
+    }
+  }
+  __device__ __forceinline__ void unpack(float (&x)[8]) const {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if constexpr (BF16) x[i] = i % 2 == 0 ? bf16_to_f32(w[i / 2] & 0xffffu) : __uint_as_float(w[i / 2] & 0xffff0000u);
+      else x[i] = __uint_as_float(w[i]);
+    }
+  }
+};
+
+// 4 consecutive output values of one token.
+template <bool BF16>
+__device__ __forceinline__ void store4(void* base, int64_t off, const f32x4& x) {
+  if constexpr (BF16) {
+    const u32x2 p = {f32_to_bf16_rne(x[0]) | (f32_to_bf16_rne(x[1]) << 16),
+                     f32_to_bf16_rne(x[2]) | (f32_to_bf16_rne(x[3]) << 16)};
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(base) + off) = p;
+  } else {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(base) + off) = x;
+  }
+}
+
+// DPP within each 16-lane row.
+template <int CTRL, bool BOUND_ZERO>
+__device__ __forceinline__ float dpp_row(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, BOUND_ZERO));
+}
+constexpr int kDppRowShr1 = 0x111;
+constexpr int kDppRowShr2 = 0x112;
+constexpr int kDppRowShr4 = 0x114;
+constexpr int kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x15F;   // row_newbcast:15, lane 15 of the row to all
+
+// inclusive prefix sum over the 16 lanes of each row
+__device__ __forceinline__ float row_scan(float x) {
+  x += dpp_row<kDppRowShr1, true>(x);
+  x += dpp_row<kDppRowShr2, true>(x);
+  x += dpp_row<kDppRowShr4, true>(x);
+  x += dpp_row<kDppRowShr8, true>(x);
+  return x;
+}
+
+// sum over the four lanes lane % 16 + 16 q, q = 0..3 (the other rows)
+__device__ __forceinline__ float cross_row_sum(float x) {
+  x = swap16_add(x, x);
+  return swap32_add(x, x);
+}
+
+// ---------------------------------------------------------------------------
+// LDS of one workgroup
+// ---------------------------------------------------------------------------
+
+template <int DK, int NW, int PREC>
+struct alignas(16) ChunkShared {
+  // published by every wave for its channels, read by all after the barrier
+  RowTable<PREC, DK> kt;          // Kt_raw = k exp(Gamma)
+  RowTable<PREC, DK> qt;          // Qt_raw = q exp(Gamma)
+  float kup[DK][kPT];             // Kup_raw^T [channel][token] = k exp(Gamma_last - Gamma)
+  float egl[DK];                  // exp(Gamma_last)
+  float beta[kChunk];
+  float nq[kChunk][4];            // per-wave partial sums of q^2, k^2 [token][wave]
+  float nk[kChunk][4];
+  float pp[NW][kChunk][kPT];      // P_raw partial of wave w, transposed: [s][t]
+  float rr[NW][kChunk][kPT];      // R_raw partial of wave w: [t][s]
+  // private to each wave
+  float lt[NW][kChunk][kPT];      // L^T: [s][t]
+  float tw[NW][kChunk][kPT];      // T = (I + L)^-1: [t][c]
+  float pq[NW][kChunk][36];       // raw q, k and Gamma of the wave's channel
+  float pk[NW][kChunk][36];       //   group, for the pair-by-pair P and R
+  float pg[NW][kChunk][36];
+};
+
+// Raw inputs of one chunk for one lane: per channel group pass, q, k and
+// the gate pre-activation of token lane % 16 at 8 channels; the value slab's
+// 8 columns and the beta logit of that token.
+template <int NP, bool QBF16>
+struct ChunkInputs {
+  Run8<QBF16> q[NP], k[NP];
+  Run8<false> x[NP];
+  Run8<QBF16> v;
+  float bl;
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      q[p].zero();
+      k[p].zero();
+      x[p].zero();
+    }
+    v.zero();
+    bl = 0.0f;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// the kernel
+// ---------------------------------------------------------------------------
+
+template <int DK, int DV, bool QBF16, bool SBF16, bool VFIRST, int PREC>
+__global__ void __launch_bounds__(DV / 32 * kWave)
+kda_prefill_chunks(DecodeArgs a) {
+  constexpr int NW = DV / 32;            // waves: one 32-value slab each
+  constexpr int NG = DK / 32;            // channel groups of 32
+  constexpr int NP = (NG + NW - 1) / NW; // channel group passes per wave
+  constexpr int MT = DK / 16;            // state row tiles
+  constexpr int KS = DK / 32;            // K = 32 steps over the channels
+  using Shared = ChunkShared<DK, NW, PREC>;
+
+  __shared__ Shared sh;
+
+  const int lane = threadIdx.x % kWave;
+  const int w = threadIdx.x / kWave;
+  const int n = lane % 16;               // token / accumulator column
+  const int g = lane / 16;               // channel quarter / accumulator row group
+
+  const int b = blockIdx.x / a.HV;
+  const int hv = blockIdx.x - b * a.HV;
+  const int h = hv / a.G;
+  int t0 = a.cu_seqlens[b];
+  int t1 = a.cu_seqlens[b + 1];
+  t0 = t0 < 0 ? 0 : (t0 > a.T ? a.T : t0);
+  t1 = t1 < t0 ? t0 : (t1 > a.T ? a.T : t1);
+  if (t1 == t0) return;
+  const int slot = a.state_indices[b];
+  const int vcol0 = 32 * w;
+
+  if (slot < 0 || slot >= a.N) {   // skipped request: zero rows, no state access
+    for (int t = t0; t < t1; ++t)
+      if (lane < 32) store_elem<QBF16>(a.out, (static_cast<int64_t>(t) * a.HV + hv) * DV + vcol0 + lane, 0.0f);
+    return;
+  }
+
+  // ---- the state slab into the accumulators: S[mt][nt][i] is
+  // S[16 mt + 4g + i][vcol0 + 16 nt + n]
+  f32x4 S[MT][2];
+  const int64_t tile = (static_cast<int64_t>(slot) * a.HV + hv) * DK * DV;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d = 16 * mt + 4 * g + i, v = vcol0 + 16 * nt + n;
+        const int64_t off = VFIRST ? static_cast<int64_t>(v) * DK + d : static_cast<int64_t>(d) * DV + v;
+        S[mt][nt][i] = load_elem<SBF16>(a.state_pool, tile + off);
+      }
+
+  // channel groups of this wave: group w + NW p covers channels
+  // [32 (w + NW p), +32); this lane's 8 start at chan0[p]
+  float dtb[NP][8];
+  int chan0[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int gi = w + NW * p;
+    chan0[p] = 32 * gi + 8 * g;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      dtb[p][j] = gi < NG ? a.dt_bias[static_cast<int64_t>(hv) * DK + chan0[p] + j] : 0.0f;
+  }
+  const float amp = exp_f(a.a_log[hv]);
+
+  auto load_inputs = [&](ChunkInputs<NP, QBF16>& in, int c0) {
+    in.zero();
+    const int64_t tok = static_cast<int64_t>(c0) + n;
+    if (tok < t1) {
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        if (w + NW * p < NG) {
+          const int64_t qk_off = (tok * a.H + h) * DK + chan0[p];
+          in.q[p].load(a.q, qk_off);
+          in.k[p].load(a.k, qk_off);
+          in.x[p].load(a.raw_gate, (tok * a.HV + hv) * DK + chan0[p]);
+        }
+      }
+      in.v.load(a.v, (tok * a.HV + hv) * DV + vcol0 + 8 * g);
+      in.bl = a.beta_logits[tok * a.HV + hv];
+    }
+  };
+
+  ChunkInputs<NP, QBF16> cur;
+  load_inputs(cur, t0);
+
+  for (int c0 = t0; c0 < t1; c0 += kChunk) {
+    const int m = t1 - c0 < kChunk ? t1 - c0 : kChunk;
+    const bool live = n < m;
+
+    ChunkInputs<NP, QBF16> nxt;        // next chunk's inputs, in flight meanwhile
+    if (c0 + kChunk < t1) load_inputs(nxt, c0 + kChunk);
+    else nxt.zero();
+
+    // ================= stage E: this wave's channels, lane = (token n, quarter g)
+    float sq = 0.0f, sk = 0.0f;
+    f32x4 Pp = {0.0f, 0.0f, 0.0f, 0.0f};   // P_raw partial (acc: rows t, column s)
+    f32x4 Rp = {0.0f, 0.0f, 0.0f, 0.0f};   // R_raw^T partial (acc: rows s, column t)
+    float pw[4] = {0.0f, 0.0f, 0.0f, 0.0f}, rw[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    bool any_wide = false;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      if (w + NW * p >= NG) continue;
+      float q[8], k[8], x[8];
+      cur.q[p].unpack(q);
+      cur.k[p].unpack(k);
+      cur.x[p].unpack(x);
+      float G[8], GL[8];
+      bool wide_lane = false;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        sq = fmaf(q[j], q[j], sq);
+        sk = fmaf(k[j], k[j], sk);
+        const float xx = x[j] + dtb[p][j];
+        const float gj = a.gate_mode == KDA_GATE_SOFTPLUS ? -amp * softplus_f(xx)
+                                                          : a.lower_bound * sigmoid_f(amp * xx);
+        G[j] = row_scan(live ? gj : 0.0f);
+        GL[j] = dpp_row<kDppRowBcast15, false>(G[j]);
+        wide_lane |= -GL[j] > kSafeSpan;
+      }
+      float kt[8], qt[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float eg = exp_f(G[j]);
+        kt[j] = k[j] * eg;
+        qt[j] = q[j] * eg;
+        sh.kup[chan0[p] + j][n] = k[j] * exp_f(GL[j] - G[j]);
+      }
+      sh.kt.store8(n, chan0[p], kt);
+      sh.qt.store8(n, chan0[p], qt);
+      if (n == 0) {
+        *reinterpret_cast<f32x4*>(&sh.egl[chan0[p]]) =
+            f32x4{exp_f(GL[0]), exp_f(GL[1]), exp_f(GL[2]), exp_f(GL[3])};
+        *reinterpret_cast<f32x4*>(&sh.egl[chan0[p] + 4]) =
+            f32x4{exp_f(GL[4]), exp_f(GL[5]), exp_f(GL[6]), exp_f(GL[7])};
+      }
+      if (!__any(wide_lane)) {
+        // this group's P and R parts as one product each
+        float kp[8], qp[8], ks[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float ep = exp_f(G[j] - 0.5f * GL[j]);
+          kp[j] = k[j] * ep;
+          qp[j] = q[j] * ep;
+          ks[j] = k[j] * __builtin_amdgcn_rcpf(ep);
+        }
+        const Frag<PREC, 8> fkp = make_frag<PREC, 8>(kp);
+        const Frag<PREC, 8> fks = make_frag<PREC, 8>(ks);
+        const Frag<PREC, 8> fqp = make_frag<PREC, 8>(qp);
+        mma(Pp, fkp, fks);    // P[t][s] = Kp[t] . Ks[s]
+        mma(Rp, fks, fqp);    // R^T[s][t] = Ks[s] . Qp[t]
+      } else {
+        // pair by pair through the wave's scratch rows
+        *reinterpret_cast<f32x4*>(&sh.pq[w][n][8 * g]) = f32x4{q[0], q[1], q[2], q[3]};
+        *reinterpret_cast<f32x4*>(&sh.pq[w][n][8 * g + 4]) = f32x4{q[4], q[5], q[6], q[7]};
+        *reinterpret_cast<f32x4*>(&sh.pk[w][n][8 * g]) = f32x4{k[0], k[1], k[2], k[3]};
+        *reinterpret_cast<f32x4*>(&sh.pk[w][n][8 * g + 4]) = f32x4{k[4], k[5], k[6], k[7]};
+        *reinterpret_cast<f32x4*>(&sh.pg[w][n][8 * g]) = f32x4{G[0], G[1], G[2], G[3]};
+        *reinterpret_cast<f32x4*>(&sh.pg[w][n][8 * g + 4]) = f32x4{G[4], G[5], G[6], G[7]};
+        wave_lds_order();
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int pi = lane + 64 * r;
+          const int tt = pi / kChunk, ss = pi % kChunk;
+          if (ss <= tt) {
+            float pv = 0.0f, rv = 0.0f;
+            for (int d = 0; d < 32; d += 4) {
+              const f32x4 kt4 = *reinterpret_cast<const f32x4*>(&sh.pk[w][tt][d]);
+              const f32x4 qt4 = *reinterpret_cast<const f32x4*>(&sh.pq[w][tt][d]);
+              const f32x4 gt4 = *reinterpret_cast<const f32x4*>(&sh.pg[w][tt][d]);
+              const f32x4 ks4 = *reinterpret_cast<const f32x4*>(&sh.pk[w][ss][d]);
+              const f32x4 gs4 = *reinterpret_cast<const f32x4*>(&sh.pg[w][ss][d]);
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const float e = ks4[j] * exp_f(fminf(gt4[j] - gs4[j], 0.0f));
+                pv = fmaf(kt4[j], e, pv);
+                rv = fmaf(qt4[j], e, rv);
+              }
+            }
+            pw[r] += pv;
+            rw[r] += rv;
+          }
+        }
+        wave_lds_order();
+        any_wide = true;
+      }
+    }
+    // publish the partials
+    sq = cross_row_sum(sq);
+    sk = cross_row_sum(sk);
+    if (g == 0) {
+      sh.nq[n][w] = sq;
+      sh.nk[n][w] = sk;
+      if (w == 0) sh.beta[n] = live ? sigmoid_f(cur.bl) : 0.0f;
+    }
+    *reinterpret_cast<f32x4*>(&sh.pp[w][n][4 * g]) = Pp;   // pp[s = n][t = 4g + i]
+    *reinterpret_cast<f32x4*>(&sh.rr[w][n][4 * g]) = Rp;   // rr[t = n][s = 4g + i]
+    if (any_wide) {
+      wave_lds_order();
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int pi = lane + 64 * r;
+        const int tt = pi / kChunk, ss = pi % kChunk;
+        if (ss <= tt) {
+          sh.pp[w][ss][tt] += pw[r];
+          sh.rr[w][tt][ss] += rw[r];
+        }
+      }
+    }
+    lds_barrier();
+
+    // ================= per wave: norms, L, T, then the slab's products
+    float rk[4], br[4];
+    {
+      const f32x4 bt = *reinterpret_cast<const f32x4*>(&sh.beta[4 * g]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x4 pk4 = *reinterpret_cast<const f32x4*>(&sh.nk[4 * g + i][0]);
+        float s2 = 0.0f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) s2 += pk4[ww];
+        rk[i] = rsqrt_f(s2 + a.l2_eps);
+        br[i] = bt[i] * rk[i];
+      }
+    }
+    float rkn, rqn;
+    {
+      const f32x4 pk4 = *reinterpret_cast<const f32x4*>(&sh.nk[n][0]);
+      const f32x4 pq4 = *reinterpret_cast<const f32x4*>(&sh.nq[n][0]);
+      float s2k = 0.0f, s2q = 0.0f;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) {
+        s2k += pk4[ww];
+        s2q += pq4[ww];
+      }
+      rkn = rsqrt_f(s2k + a.l2_eps);
+      rqn = a.scale * rsqrt_f(s2q + a.l2_eps);
+    }
+    // L[t][s] for rows t = 4g + i, column s = n, stored transposed
+    {
+      f32x4 Pf = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) Pf += *reinterpret_cast<const f32x4*>(&sh.pp[ww][n][4 * g]);
+      const float cs = rkn * sh.beta[n];
+      f32x4 Lv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Lv[i] = n < 4 * g + i ? rk[i] * cs * Pf[i] : 0.0f;
+      *reinterpret_cast<f32x4*>(&sh.lt[w][n][4 * g]) = Lv;
+    }
+    wave_lds_order();
+    // T = (I + L)^-1, column c = n: right-looking substitution (the rows'
+    // updates are independent, so only one multiply-add per row is serial)
+    {
+      float xs[kChunk];
+#pragma unroll
+      for (int t = 0; t < kChunk; ++t) xs[t] = t == n ? 1.0f : 0.0f;
+#pragma unroll
+      for (int s = 0; s < kChunk; ++s) {
+        if (g == 0) sh.tw[w][s][n] = xs[s];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          if (4 * q4 + 3 <= s) continue;
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sh.lt[w][s][4 * q4]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (4 * q4 + j > s) xs[4 * q4 + j] = fmaf(-l4[j], xs[s], xs[4 * q4 + j]);
+        }
+      }
+    }
+    // R_raw as the B operand of R_raw^T: lane (t = n, g) holds R[t][4g + j]
+    Frag<PREC, 4> fr;
+    {
+      f32x4 Rf = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) Rf += *reinterpret_cast<const f32x4*>(&sh.rr[ww][n][4 * g]);
+      float rv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) rv[j] = 4 * g + j <= n ? Rf[j] : 0.0f;
+      fr = make_frag<PREC, 4>(rv);
+    }
+
+    // X = V - diag(rk) Kt_raw S,  Y^T = S^T Qt_raw^T   (per value tile nt)
+    f32x4 X[2], YT[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) X[nt] = YT[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const Frag<PREC, 8> fk = sh.kt.frag8(n, s, g);
+      const Frag<PREC, 8> fq = sh.qt.frag8(n, s, g);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const Frag<PREC, 8> fs = acc_frag8<PREC>(S[2 * s][nt], S[2 * s + 1][nt]);
+        mma(X[nt], fk, fs);
+        mma(YT[nt], fs, fq);
+      }
+    }
+    {
+      float vv[8];
+      cur.v.unpack(vv);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) X[nt][i] *= -rk[i];
+        mma_identity<PREC, QBF16>(X[nt], vv, nt, n, g);
+      }
+    }
+    wave_lds_order();
+
+    // U = T X, U' = diag(beta rk) U, O^T = diag(rq)(Y^T + U'^T R_raw^T),
+    // S = diag(exp(Gamma_last)) S + Kup_raw^T U'
+    const f32x4 t4 = *reinterpret_cast<const f32x4*>(&sh.tw[w][n][4 * g]);
+    const Frag<PREC, 4> ft = acc_frag4<PREC>(t4);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      f32x4 U = {0.0f, 0.0f, 0.0f, 0.0f};
+      mma(U, ft, acc_frag4<PREC>(X[nt]));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) U[i] *= br[i];
+      const Frag<PREC, 4> fu = acc_frag4<PREC>(U);
+      f32x4 OT = YT[nt];
+      mma(OT, fu, fr);
+      if (live) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) OT[i] *= rqn;
+        store4<QBF16>(a.out, (static_cast<int64_t>(c0 + n) * a.HV + hv) * DV + vcol0 + 16 * nt + 4 * g, OT);
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const f32x4 e = *reinterpret_cast<const f32x4*>(&sh.egl[16 * mt + 4 * g]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[mt][nt][i] *= e[i];
+        const f32x4 k4 = *reinterpret_cast<const f32x4*>(&sh.kup[16 * mt + n][4 * g]);
+        mma(S[mt][nt], acc_frag4<PREC>(k4), fu);
+      }
+    }
+    lds_barrier();   // the shared tables are rewritten by the next chunk
+    cur = nxt;
+  }
+
+  // ---- the advanced state back to its slot
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d = 16 * mt + 4 * g + i, v = vcol0 + 16 * nt + n;
+        const int64_t off = VFIRST ? static_cast<int64_t>(v) * DK + d : static_cast<int64_t>(d) * DV + v;
+        store_elem<SBF16>(a.state_pool, tile + off, S[mt][nt][i]);
+      }
+}
+
+// ---------------------------------------------------------------------------
+// dispatch
+// ---------------------------------------------------------------------------
+
+template <int DK, int DV, bool QBF16, bool SBF16, bool VFIRST, int PREC>
+int launch_one(const DecodeArgs& a, hipStream_t stream) {
+  const int64_t grid = static_cast<int64_t>(a.B) * a.HV;
+  hipLaunchKernelGGL((kda_prefill_chunks<DK, DV, QBF16, SBF16, VFIRST, PREC>),
+                     dim3(static_cast<uint32_t>(grid)), dim3(DV / 32 * kWave), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+template <int DK, int DV, bool QBF16, bool SBF16, bool VFIRST>
+int pick_prec(const DecodeArgs& a, int prec, hipStream_t s) {
+  return prec == KDA_MATMUL_F32 ? launch_one<DK, DV, QBF16, SBF16, VFIRST, KDA_MATMUL_F32>(a, s)
+                                : launch_one<DK, DV, QBF16, SBF16, VFIRST, KDA_MATMUL_SPLIT_BF16>(a, s);
+}
+
+template <int DK, int DV>
+int pick_types(const DecodeArgs& a, bool qbf16, bool sbf16, bool vfirst, int prec, hipStream_t s) {
+  if (qbf16) {
+    if (sbf16) return vfirst ? pick_prec<DK, DV, true, true, true>(a, prec, s) : pick_prec<DK, DV, true, true, false>(a, prec, s);
+    return vfirst ? pick_prec<DK, DV, true, false, true>(a, prec, s) : pick_prec<DK, DV, true, false, false>(a, prec, s);
+  }
+  if (sbf16) return vfirst ? pick_prec<DK, DV, false, true, true>(a, prec, s) : pick_prec<DK, DV, false, true, false>(a, prec, s);
+  return vfirst ? pick_prec<DK, DV, false, false, true>(a, prec, s) : pick_prec<DK, DV, false, false, false>(a, prec, s);
+}
+
+template <int DK>
+int pick_dv(const DecodeArgs& a, int dv, bool qbf16, bool sbf16, bool vfirst, int prec, hipStream_t s) {
+  switch (dv) {
+    case 32: return pick_types<DK, 32>(a, qbf16, sbf16, vfirst, prec, s);
+    case 64: return pick_types<DK, 64>(a, qbf16, sbf16, vfirst, prec, s);
+    case 128: return pick_types<DK, 128>(a, qbf16, sbf16, vfirst, prec, s);
+    default: return KDA_ERR_UNSUPPORTED;
+  }
+}
+
+}  // namespace
+
+int launch_prefill(const DecodeArgs& args, int dk, int dv, bool qkv_bf16, bool state_bf16,
+                   int state_layout, int matmul, hipStream_t stream) {
+  const bool vfirst = state_layout == KDA_STATE_V_FIRST;
+  switch (dk) {
+    case 32: return pick_dv<32>(args, dv, qkv_bf16, state_bf16, vfirst, matmul, stream);
+    case 64: return pick_dv<64>(args, dv, qkv_bf16, state_bf16, vfirst, matmul, stream);
+    case 128: return pick_dv<128>(args, dv, qkv_bf16, state_bf16, vfirst, matmul, stream);
+    default: return KDA_ERR_UNSUPPORTED;
+  }
+}
+
+}  // namespace kda

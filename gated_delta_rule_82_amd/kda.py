@@ -1,6 +1,6 @@
 """Thin ctypes binding of libkda (argument marshalling only).
 
-Every step of the decode runs in the HIP library; this module turns torch
+Every step of the decode and of the chunked prefill runs in the HIP library; this module turns torch
 device tensors into ``kda_tensor`` descriptors, passes the current HIP stream
 and raises :class:`KdaError` on a nonzero status.  There is no fallback: if
 the library is missing or a tensor is not on a GPU, the call raises.
@@ -36,8 +36,12 @@ KDA_STATE_K_FIRST = 0
 KDA_STATE_V_FIRST = 1
 STATE_LAYOUTS = {"k_first": KDA_STATE_K_FIRST, "v_first": KDA_STATE_V_FIRST}
 
-EXPORTED_SYMBOLS = ("kda_decode", "kda_decode_conv", "kda_check_host", "kda_status_string",
-                    "kda_abi_version")
+KDA_MATMUL_SPLIT_BF16 = 0
+KDA_MATMUL_F32 = 1
+MATMULS = {"split_bf16": KDA_MATMUL_SPLIT_BF16, "f32": KDA_MATMUL_F32}
+
+EXPORTED_SYMBOLS = ("kda_decode", "kda_decode_conv", "kda_prefill", "kda_check_host",
+                    "kda_status_string", "kda_abi_version")
 CONV_FIELDS = ("x_q", "x_k", "x_v", "w_q", "w_k", "w_v", "win_q", "win_k", "win_v", "q_conv",
                "k_conv")
 
@@ -90,6 +94,9 @@ def library() -> ctypes.CDLL:
     lib.kda_decode_conv.argtypes = [P, ctypes.POINTER(KdaConv)] + [P] * 7 + [ctypes.POINTER(KdaMode),
                                                                         ctypes.c_void_p]
     lib.kda_decode_conv.restype = ctypes.c_int
+    lib.kda_prefill.argtypes = [P] * 11 + [ctypes.POINTER(KdaMode), ctypes.c_int32,
+                                            ctypes.c_void_p]
+    lib.kda_prefill.restype = ctypes.c_int
     lib.kda_check_host.argtypes = [ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
                                    ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
     lib.kda_check_host.restype = ctypes.c_int
@@ -132,6 +139,16 @@ def call_raw(tensors, mode: KdaMode, stream: int = 0) -> int:
     ptrs = [ctypes.byref(t) if t is not None else None for t in tensors]
     return lib.kda_decode(*ptrs, ctypes.byref(mode) if mode is not None else None,
                           ctypes.c_void_p(stream))
+
+
+def call_raw_prefill(tensors, mode: KdaMode, matmul: int = KDA_MATMUL_SPLIT_BF16,
+                     stream: int = 0) -> int:
+    """Call kda_prefill on 11 prepared descriptors (None passes NULL); returns
+    the status code without raising."""
+    lib = library()
+    ptrs = [ctypes.byref(t) if t is not None else None for t in tensors]
+    return lib.kda_prefill(*ptrs, ctypes.byref(mode) if mode is not None else None,
+                           ctypes.c_int32(matmul), ctypes.c_void_p(stream))
 
 
 def call_raw_conv(out, conv, rest, mode: KdaMode, stream: int = 0) -> int:
@@ -188,6 +205,30 @@ def decode(out, q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens, stat
         rc = call_raw(descs, mode, stream)
     if rc != KDA_OK:
         raise KdaError(rc)
+
+
+def prefill(out, q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens, state_pool,
+            state_indices, *, gate_mode="softplus", lower_bound=0.0, l2_eps=0.0, scale=0.0,
+            state_layout="k_first", matmul="split_bf16", stream: Optional[int] = None) -> None:
+    """The recurrence over long requests in chunks of 16 tokens on the matrix
+    cores (kda_prefill in include/kda.h): same tensors and result as
+    :func:`decode`; ``matmul`` is "split_bf16" (default) or "f32"."""
+    import torch
+    tensors = (out, q, k, v, raw_gate, beta_logits, a_log, dt_bias, cu_seqlens, state_pool,
+               state_indices)
+    descs = [_descriptor(t, n) for t, n in zip(tensors, ARG_NAMES)]
+    dev = q.device
+    for t, n in zip(tensors, ARG_NAMES):
+        if t.device != dev:
+            raise ValueError(f"{n}: on {t.device}, expected {dev}")
+    mode = make_mode(gate_mode, lower_bound, l2_eps, scale, state_layout)
+    mm = MATMULS[matmul] if isinstance(matmul, str) else int(matmul)
+    with torch.cuda.device(dev):
+        if stream is None:
+            stream = torch.cuda.current_stream(dev).cuda_stream
+        rc = call_raw_prefill(descs, mode, mm, stream)
+    if rc != KDA_OK:
+        raise KdaError(rc, "kda_prefill")
 
 
 def check_host(cu_seqlens, state_indices, T: int, n_slots: int) -> int:

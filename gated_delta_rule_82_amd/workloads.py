@@ -7,7 +7,8 @@ their inputs from here, and the benchmark draws its workload from here too.
 The presets mirror the decode workloads the pages describe: a 96-head layer
 with dk = dv = 128 ("Delta-rule write" page, input/output shapes), the
 Kimi-Linear 32-head shape, a GQA/varlen speculative-window batch and a tiny
-dk = 16 case.  Distributions: q, k, v, raw_gate, beta_logits ~ N(0, 1);
+dk = 16 case; plus one whole-sequence (prefill) batch of the 96-head layer
+(the same page in prefill mode: [B, 96, T, 128] inputs).  Distributions: q, k, v, raw_gate, beta_logits ~ N(0, 1);
 A_log ~ U(0, ln 16); dt_bias ~ N(0, 0.1); state ~ N(0, sigma).
 
 Draw order from ``numpy.random.default_rng(seed)`` (fixed, so every consumer
@@ -84,7 +85,16 @@ PRESETS = {
         name="stress_b1024_n4", B=1024, H=96, HV=96, DK=128, DV=128,
         n_slots=2048, tokens="4", gate_mode=LOWER_BOUND, lower_bound=-5.0,
         description="B=1024, 4 tokens, 96 heads, lower-bound gate"),
+    # whole-sequence (prefill) workload of the 96-head layer, as the model
+    # runs it: value-first state, lower-bound gate
+    "prefill_b8_t2048_h96": Workload(
+        name="prefill_b8_t2048_h96", B=8, H=96, HV=96, DK=128, DV=128, n_slots=16,
+        tokens="2048", gate_mode=LOWER_BOUND, lower_bound=-5.0, state_layout="v_first",
+        description="prefill: B=8 x 2048 tokens, 96 heads, dk=dv=128, bf16, lower-bound gate, "
+                    "value-first fp32 state"),
 }
+
+PREFILL_HEADLINE = "prefill_b8_t2048_h96"
 
 HEADLINE = "wide_b256_h96"
 

@@ -54,7 +54,7 @@ extern "C" {
 /* hipStream_t, declared here so that this header needs no HIP include. */
 typedef struct ihipStream_t* hipStream_t;
 
-#define KDA_ABI_VERSION 3
+#define KDA_ABI_VERSION 4
 
 /* Status codes.  Zero is success; errors are negative. */
 enum kda_status {
@@ -87,6 +87,13 @@ enum kda_gate_mode {
 enum kda_state_layout {
   KDA_STATE_K_FIRST = 0,    /* [dk][dv]: S[k][v] (the default)             */
   KDA_STATE_V_FIRST = 1     /* [dv][dk]: the transposed layout             */
+};
+
+/* Matrix precision of kda_prefill. */
+enum kda_matmul {
+  KDA_MATMUL_SPLIT_BF16 = 0, /* each fp32 operand as hi + lo bf16, three bf16 */
+                             /* products per fp32 product (the default)       */
+  KDA_MATMUL_F32 = 1         /* the fp32 matrix instructions                  */
 };
 
 /* A dense row-major tensor: `data` points at element [0,...,0]; the extents
@@ -197,6 +204,37 @@ int kda_decode_conv(const kda_tensor* out, const kda_conv* conv, const kda_tenso
                     const kda_tensor* dt_bias, const kda_tensor* cu_seqlens,
                     const kda_tensor* state_pool, const kda_tensor* state_indices,
                     const kda_mode* mode, hipStream_t stream);
+
+/*
+ * kda_prefill - the same operation and arguments as kda_decode, computed
+ * for long requests: each (request, value head) walks its tokens in chunks
+ * of 16 on the matrix cores, and the result equals the token-by-token
+ * recurrence up to rounding order.  The model runs its whole-sequence step
+ * this way (chunk_kda, "Delta-rule write" page, modeling_kimi_linear.py
+ * excerpt; the pages leave that kernel's internals open, so only the
+ * recurrence's result is fixed).  Per chunk, with Gamma the running sum of
+ * the log-decays since the chunk start and S0 the state before it:
+ *     U = (I + L)^-1 (V - (kh o exp(Gamma)) S0)         (the corrections)
+ *     O = (qh o exp(Gamma)) S0 + R' U
+ *     S = diag(exp(Gamma_last)) S0 + Kup^T U
+ * where L and R' hold the decayed key-key and query-key products of the
+ * chunk scaled by beta (strictly lower and lower triangular), and
+ * Kup = beta kh o exp(Gamma_last - Gamma).
+ *
+ * dk and dv must each be 32, 64 or 128 (else KDA_ERR_UNSUPPORTED).
+ * `matmul` is an enum kda_matmul (else KDA_ERR_MODE): the split-bf16 form
+ * keeps 16 significant bits per operand; KDA_MATMUL_F32 gives fp32
+ * products at about three times the matrix time.  The kernel needs no
+ * workspace: each workgroup keeps its state slab in registers and the
+ * chunk's operands in LDS.  Preconditions, conventions (skipped and empty
+ * requests) and errors are those of kda_decode.
+ */
+int kda_prefill(const kda_tensor* out, const kda_tensor* q, const kda_tensor* k,
+                const kda_tensor* v, const kda_tensor* raw_gate,
+                const kda_tensor* beta_logits, const kda_tensor* a_log,
+                const kda_tensor* dt_bias, const kda_tensor* cu_seqlens,
+                const kda_tensor* state_pool, const kda_tensor* state_indices,
+                const kda_mode* mode, int32_t matmul, hipStream_t stream);
 
 /*
  * kda_check_host - validate host copies of the decode metadata.

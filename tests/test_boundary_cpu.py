@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = kda.library()
-    assert lib.kda_abi_version() == 3
+    assert lib.kda_abi_version() == 4
     codes = [kda.KDA_OK, kda.KDA_ERR_NULL, kda.KDA_ERR_DTYPE, kda.KDA_ERR_SHAPE,
              kda.KDA_ERR_UNSUPPORTED, kda.KDA_ERR_MODE, kda.KDA_ERR_LAUNCH,
              kda.KDA_ERR_PRECONDITION]
@@ -275,3 +275,45 @@ def test_conv_dtype_and_shape_errors():
     # the recurrence arguments are checked as in kda_decode
     d, conv = conv_descriptors()
     assert call_conv(d, conv, gate_mode="lower_bound", lower_bound=1.0) == kda.KDA_ERR_MODE
+
+
+# ---------------------------------------------------------------------------
+# kda_prefill: the decode checks, plus the matmul selector and head sizes
+# ---------------------------------------------------------------------------
+
+def call_prefill(descs, matmul=kda.KDA_MATMUL_SPLIT_BF16, mode=None, **mode_kw):
+    if mode is None:
+        mode = kda.make_mode(**mode_kw)
+    return kda.call_raw_prefill([descs[n] for n in kda.ARG_NAMES], mode, matmul, 0)
+
+
+def test_prefill_nothing_to_do_and_nulls():
+    assert call_prefill(descriptors(B=0, T=0)) == kda.KDA_OK
+    assert call_prefill(descriptors(B=3, T=0), matmul=kda.KDA_MATMUL_F32) == kda.KDA_OK
+    d = descriptors(B=0, T=0)
+    assert kda.call_raw_prefill([d[n] for n in kda.ARG_NAMES], None, 0, 0) == kda.KDA_ERR_NULL
+    for n in kda.ARG_NAMES:
+        e = dict(d)
+        e[n] = None
+        assert call_prefill(e) == kda.KDA_ERR_NULL, n
+
+
+@pytest.mark.parametrize("matmul", [-1, 2, 7])
+def test_prefill_rejects_unknown_matmul(matmul):
+    assert call_prefill(descriptors(B=0, T=0), matmul=matmul) == kda.KDA_ERR_MODE
+
+
+@pytest.mark.parametrize("dk,dv", [(16, 128), (128, 16), (16, 16)])
+def test_prefill_rejects_head_size_16(dk, dv):
+    # decode takes 16; the chunked kernel needs whole 32-wide operand slices
+    assert call(descriptors(B=0, T=0, DK=dk, DV=dv)) == kda.KDA_OK
+    assert call_prefill(descriptors(B=0, T=0, DK=dk, DV=dv)) == kda.KDA_ERR_UNSUPPORTED
+
+
+def test_prefill_shares_the_decode_checks():
+    d = descriptors()
+    e = dict(d)
+    e["v"] = reshape(d["v"], (1, 4, 4, 128))              # T disagrees with q
+    assert call_prefill(e) == kda.KDA_ERR_SHAPE
+    assert call_prefill(d, gate_mode=7) == kda.KDA_ERR_MODE
+    assert call_prefill(d, gate_mode="lower_bound", lower_bound=0.5) == kda.KDA_ERR_MODE

@@ -1,0 +1,103 @@
+"""GPU parity of the chunked prefill (kda_prefill, through the C ABI)
+against the fp64 oracle's token loop.
+
+Every case runs both matrix precisions.  Tolerances: the required bounds of
+tests/kda_harness.py and its PREFILL_TOL tight bounds.  Each case prints its
+name and shape before it touches the GPU.
+"""
+import numpy as np
+import pytest
+
+from gated_delta_rule_82_amd import workloads as wl
+from tests import kda_harness as H
+
+pytestmark = pytest.mark.gpu
+
+MATMULS = ("split_bf16", "f32")
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from gated_delta_rule_82_amd import kda
+    kda.library()
+    return torch
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def work(name, B=3, H_=2, HV=4, DK=32, DV=32, tokens="u:0..40", qkv="bf16", gate=wl.LOWER_BOUND,
+         lb=-5.0, seed=0, slots=None, **kw):
+    return wl.Workload(name=name, B=B, H=H_, HV=HV, DK=DK, DV=DV,
+                       n_slots=slots if slots is not None else 2 * B + 3, tokens=tokens,
+                       qkv_dtype=qkv, gate_mode=gate, lower_bound=lb if gate == wl.LOWER_BOUND else 0.0,
+                       seed=seed, host_state=True, **kw)
+
+
+CASES = {
+    # ragged chunks (37 = 2*16 + 5), an exact chunk, a short request; GQA
+    "d32_gqa_ragged": work("d32_gqa_ragged", cu_seqlens=(0, 37, 53, 58), qkv="f32"),
+    # softplus gate: decay spans beyond the one-product bound (pairwise P, R)
+    "d32_softplus": work("d32_softplus", cu_seqlens=(0, 37, 53, 58), qkv="f32", gate=wl.SOFTPLUS),
+    "d64_bf16_varlen": work("d64_bf16_varlen", B=6, H_=4, HV=4, DK=64, DV=64, tokens="u:0..70", lb=-2.0,
+                            seed=1),
+    "d128_vfirst": work("d128_vfirst", B=2, H_=2, HV=2, DK=128, DV=128, tokens="u:100..300", seed=2,
+                        state_layout="v_first"),
+    "d128_kfirst_softplus": work("d128_kfirst_softplus", B=2, H_=1, HV=2, DK=128, DV=128,
+                                 tokens="u:40..90", gate=wl.SOFTPLUS, seed=3),
+    "d128_bf16_state": work("d128_bf16_state", B=3, H_=2, HV=2, DK=128, DV=128, tokens="u:1..80", seed=4,
+                            state_dtype="bf16", state_layout="v_first"),
+    "d64_dv128": work("d64_dv128", B=3, H_=2, HV=2, DK=64, DV=128, tokens="u:10..60", seed=5),
+    "d128_dv32": work("d128_dv32", B=3, H_=2, HV=4, DK=128, DV=32, tokens="u:10..60", seed=6,
+                      qkv="f32", state_layout="v_first"),
+    "d32_dv64_bf16state_kfirst": work("d32_dv64_bf16state_kfirst", B=4, H_=2, HV=2, DK=32, DV=64,
+                                      tokens="u:0..50", seed=7, state_dtype="bf16"),
+    # skipped requests (negative index), empty requests, a one-token request
+    "skip_and_empty": work("skip_and_empty", B=5, H_=2, HV=2, DK=64, DV=64,
+                           cu_seqlens=(0, 20, 20, 41, 42, 42), state_indices=(3, 1, -1, 0, -1),
+                           slots=6, seed=8),
+}
+
+
+@pytest.mark.parametrize("matmul", MATMULS)
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_prefill_parity(torch_cuda, name, matmul):
+    cfg = CASES[name]
+    _say("prefill", name, matmul, cfg)
+    stats, _, _ = H.parity_case(wl.draw(cfg), entry="prefill", matmul=matmul)
+    print(name, matmul, stats, flush=True)
+
+
+@pytest.mark.parametrize("matmul", MATMULS)
+def test_prefill_long_request(torch_cuda, matmul):
+    """One 6000-token request (375 chunks): the error must not grow with length."""
+    cfg = work("long", B=1, H_=1, HV=2, DK=128, DV=128, tokens="6000", seed=9, state_layout="v_first")
+    _say("prefill long", matmul, cfg)
+    stats, _, _ = H.parity_case(wl.draw(cfg), entry="prefill", matmul=matmul)
+    print("long", matmul, stats, flush=True)
+
+
+def test_prefill_headline_sampled(torch_cuda):
+    """The 96-head prefill batch at full size (B=8 x 2048 tokens), in the
+    launch the benchmark times; the oracle checks 6 sampled tiles."""
+    cfg = wl.PRESETS[wl.PREFILL_HEADLINE]
+    _say("prefill headline", cfg.description)
+    stats, _, _ = H.parity_case(wl.draw(cfg), entry="prefill", sample=6, check_untouched=False)
+    print("prefill headline", stats, flush=True)
+    torch_cuda.cuda.empty_cache()
+
+
+def test_prefill_matches_decode_on_one_token_requests(torch_cuda):
+    """With one token per request the chunk is a single padded token: both
+    entry points must agree with the oracle (and closely with each other)."""
+    cfg = work("one_token", B=16, H_=4, HV=8, DK=128, DV=128, tokens="1", seed=10)
+    _say("prefill one-token", cfg)
+    inp = wl.draw(cfg)
+    _, out_p, pool_p = H.parity_case(inp, entry="prefill")
+    _, out_d, pool_d = H.parity_case(inp, entry="decode")
+    diff = float((pool_p - pool_d).abs().max()) / float(pool_d.abs().max())
+    assert diff < 3e-5, diff
