@@ -1,11 +1,20 @@
 """Benchmark of the KDA decode op on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py --prefill [--matmul split_bf16|f32]
 
 A step is one kda_decode call over one batch of the workload (default: the
 96-head layer, B=256 requests x 1 token, dk = dv = 128, bf16 q/k/v, fp32
 state pool of 512 slots).  All inputs are resident in HBM before timing.
 Prints one JSON line on stdout; progress goes to stderr.
+
+--prefill times kda_prefill instead (the chunked whole-sequence form on the
+matrix cores; default workload B=8 x 2048 tokens, 96 heads, value-first
+fp32 state): value is tokens x heads per second, and the roofline is the
+matrix one -- algorithmic flops of the chunk form (X, Y, the state update,
+U, O and the P, R products; 16-token chunks, a ragged chunk counted whole)
+over the mean kernel time, against the dense bf16 peak (split-bf16
+products) or the fp32 matrix peak.
 
 Fields beyond the common ones:
   roofline      HBM roofline of the decode kernel: achieved = algorithmic
@@ -33,24 +42,34 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "state GB/s (%HBM peak) + tokens·heads/s, KDA decode B=256 H=96 d=128"
+PREFILL_METRIC = "tokens·heads/s, KDA chunked prefill B=8 T=2048 H=96 d=128"
 HBM_PEAK_GBPS = 8000.0
-KERNEL_SOURCE = os.path.join(ROOT, "gated_delta_rule_82_amd", "csrc", "kda_decode.hip")
+MATRIX_PEAK_TFLOPS = {"split_bf16": 2500.0, "f32": 157.3}   # dense bf16 / fp32 matrix
+CSRC = os.path.join(ROOT, "gated_delta_rule_82_amd", "csrc")
+KERNEL_SOURCES = {
+    "kda_decode": [os.path.join(CSRC, "kda_decode.hip"), os.path.join(CSRC, "kda_device.h")],
+    "kda_prefill": [os.path.join(CSRC, "kda_prefill.hip"), os.path.join(CSRC, "kda_device.h")],
+}
 PROFILES = os.path.join(ROOT, "profiles")
+CHUNK = 16
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_source_hash(op: str = "kda_decode") -> str:
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES[op]:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def committed_traffic(workload: str):
-    """HBM bytes per launch from profiles/kda_decode_<workload>_counters.md, if
+def committed_traffic(workload: str, op: str = "kda_decode"):
+    """HBM bytes per launch from profiles/<op>_<workload>_counters.md, if
     that summary was taken on the current kernel source."""
-    path = os.path.join(PROFILES, f"kda_decode_{workload}_counters.md")
+    path = os.path.join(PROFILES, f"{op}_{workload}_counters.md")
     if not os.path.exists(path):
         return None, "no counter summary"
     text = open(path).read()
@@ -58,16 +77,16 @@ def committed_traffic(workload: str):
     m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
     if not (m_hash and m_bytes):
         return None, "summary lacks traffic fields"
-    if m_hash.group(1) != kernel_source_hash():
+    if m_hash.group(1) != kernel_source_hash(op):
         return None, "kernel changed since counters were taken"
     return float(m_bytes.group(1)), path
 
 
-def cpu_baseline(inp, pool_t, budget_s: float):
-    """Time the fp64 oracle on the workload's requests in order (wrapping
-    around to further passes), one BLAS thread, until about ``budget_s``
-    seconds of work are done."""
-    import numpy as np
+def cpu_baseline(inp, pool_t, budget_s: float, heads_per_step=None):
+    """Time the fp64 oracle on the workload's (request, head) tiles in order
+    (wrapping around to further passes), one BLAS thread, until about
+    ``budget_s`` seconds of work are done.  A step is up to 8 requests with
+    all their heads, or ``heads_per_step`` heads of one request."""
     from threadpoolctl import threadpool_limits
     import torch
     from oracle import kda_oracle as ko
@@ -79,14 +98,15 @@ def cpu_baseline(inp, pool_t, budget_s: float):
 
     cfg = inp.cfg
     lb = cfg.lower_bound if cfg.gate_mode == "lower_bound" else None
-    done_req, done_th, done_state, elapsed = 0, 0, 0, 0.0
+    order = [(bb, hv) for bb in range(cfg.B) for hv in range(cfg.HV)]
+    per = heads_per_step or 8 * cfg.HV
+    done_tiles, done_th, done_state, elapsed = 0, 0, 0, 0.0
     with threadpool_limits(limits=1):
-        b = 0
+        i = 0
         while elapsed < budget_s:
-            if b >= cfg.B:          # whole batch done: start another pass
-                b = 0
-            step = max(1, min(8, cfg.B - b))
-            tiles = [(bb, hv) for bb in range(b, b + step) for hv in range(cfg.HV)]
+            if i >= len(order):     # whole batch done: start another pass
+                i = 0
+            tiles = order[i:i + per]
             valid = [(bb, hv) for bb, hv in tiles if inp.state_indices[bb] >= 0]
             init = gather_tiles([int(inp.state_indices[bb]) for bb, _ in valid],
                                 [hv for _, hv in valid])
@@ -97,19 +117,21 @@ def cpu_baseline(inp, pool_t, budget_s: float):
                           gate_mode=cfg.gate_mode, lower_bound=lb, state_layout=cfg.state_layout,
                           state_dtype=cfg.state_dtype)
             elapsed += time.perf_counter() - t0
-            counts = np.diff(inp.cu_seqlens[b:b + step + 1])
-            done_th += int(counts.sum()) * cfg.HV
-            done_state += int(((counts > 0) & (inp.state_indices[b:b + step] >= 0)).sum()) \
-                * cfg.HV * 2 * cfg.DK * cfg.DV * cfg.state_elem_bytes
-            done_req += step
-            b += step
+            for bb, hv in tiles:
+                n = int(inp.cu_seqlens[bb + 1] - inp.cu_seqlens[bb])
+                done_th += n
+                if n > 0 and inp.state_indices[bb] >= 0:
+                    done_state += 2 * cfg.DK * cfg.DV * cfg.state_elem_bytes
+            done_tiles += len(tiles)
+            i += per
+    total = len(order)
     return {
         "value": round(done_state / elapsed / 1e9, 6),
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"{done_req} requests x {cfg.HV} heads ({done_req / cfg.B:.2f} passes over the "
-                  f"{cfg.B}-request batch), all their tokens: {done_th} token-heads in "
+        "sample": f"{done_tiles} (request, head) tiles ({done_tiles / total:.3f} passes over the "
+                  f"batch's {total}), all their tokens: {done_th} token-heads in "
                   f"{elapsed:.1f} s, fp64 numpy, 1 BLAS thread",
         "tokens_heads_per_s": round(done_th / elapsed, 3),
         "host_cores_available": len(os.sched_getaffinity(0)),
@@ -149,8 +171,13 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None)
-    ap.add_argument("--state-layout", choices=("k_first", "v_first"), default="k_first")
-    ap.add_argument("--state-dtype", choices=("f32", "bf16"), default="f32")
+    ap.add_argument("--state-layout", choices=("k_first", "v_first"), default=None,
+                    help="default: the workload's (key-first for the decode batches)")
+    ap.add_argument("--state-dtype", choices=("f32", "bf16"), default=None)
+    ap.add_argument("--prefill", action="store_true",
+                    help="time kda_prefill (chunked, matrix cores) on the prefill workload")
+    ap.add_argument("--matmul", choices=("split_bf16", "f32"), default="split_bf16",
+                    help="matrix precision of --prefill")
     ap.add_argument("--conv", action="store_true",
                     help="time kda_decode_conv: the step with the short convolutions in front")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
@@ -158,6 +185,9 @@ def main(argv=None) -> int:
     ap.add_argument("--no-copy-ceiling", action="store_true")
     args = ap.parse_args(argv)
 
+    if args.prefill and args.conv:
+        print("bench.py: --prefill and --conv are separate measurements", file=sys.stderr)
+        return 2
     if args.gpus != 1:
         print(f"bench.py: this KDA decode build runs on one GPU; --gpus {args.gpus} is not "
               "supported (every (request, head) tile is independent, so more GPUs would each "
@@ -174,8 +204,10 @@ def main(argv=None) -> int:
         return 1
     kda.library()     # fail loudly if the HIP library is not built
 
-    name = args.workload or wl.HEADLINE
-    cfg = wl.preset(name, state_layout=args.state_layout, state_dtype=args.state_dtype)
+    name = args.workload or (wl.PREFILL_HEADLINE if args.prefill else wl.HEADLINE)
+    over = {k: v for k, v in (("state_layout", args.state_layout), ("state_dtype", args.state_dtype))
+            if v is not None}
+    cfg = wl.preset(name, **over)
     log(f"[bench] workload {name}: {cfg.description}")
     inp = wl.draw(cfg)
     dev = wl.to_device(inp)
@@ -203,6 +235,11 @@ def main(argv=None) -> int:
                             cd["win_q"], cd["win_k"], cd["win_v"], cd["q_conv"], cd["k_conv"],
                             dev["raw_gate"], dev["beta_logits"], dev["a_log"], dev["dt_bias"],
                             dev["cu_seqlens"], pool, dev["state_indices"], stream=handle, **mode)
+    elif args.prefill:
+        def step():
+            kda.prefill(out, dev["q"], dev["k"], dev["v"], dev["raw_gate"], dev["beta_logits"],
+                        dev["a_log"], dev["dt_bias"], dev["cu_seqlens"], pool, dev["state_indices"],
+                        stream=handle, matmul=args.matmul, **mode)
     else:
         def step():
             kda.decode(out, dev["q"], dev["k"], dev["v"], dev["raw_gate"], dev["beta_logits"],
@@ -229,6 +266,10 @@ def main(argv=None) -> int:
     mean_kernel_ms = float(kernel_ms.mean())
     log(f"[bench] wall {ms_per_step * 1e3:.1f} us/step, kernel mean {mean_kernel_ms * 1e3:.1f} us "
         f"(min {kernel_ms.min() * 1e3:.1f}, max {kernel_ms.max() * 1e3:.1f})")
+
+    if args.prefill:
+        return report_prefill(args, cfg, name, inp, pool, ms_per_step, mean_kernel_ms, alg_bytes,
+                              tok_heads)
 
     value = state_b / (ms_per_step * 1e-3) / 1e9
     achieved = alg_bytes / (mean_kernel_ms * 1e-3) / 1e9
@@ -292,6 +333,81 @@ def main(argv=None) -> int:
         },
         "cpu_baseline": cpu,
         "active_tiles": int(((counts > 0) & (inp.state_indices >= 0)).sum()) * cfg.HV,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def chunk_flops(dk: int, dv: int) -> int:
+    """Algorithmic flops of one 16-token chunk of one (request, head) tile:
+    X = V - Kt S and Y = Qt S (2 C dk dv each), the state update Kup^T U
+    (2 C dk dv), U = T X and R U (2 C^2 dv each), the P and R products
+    (2 C^2 dk each)."""
+    c = CHUNK
+    return 2 * (3 * c * dk * dv + 2 * c * c * dv + 2 * c * c * dk)
+
+
+def report_prefill(args, cfg, name, inp, pool, ms_per_step, mean_kernel_ms, alg_bytes, tok_heads):
+    import numpy as np
+    counts = np.diff(inp.cu_seqlens)
+    active = (counts > 0) & (inp.state_indices >= 0)
+    chunks = int((-(-counts[active] // CHUNK)).sum()) * cfg.HV
+    flops = chunks * chunk_flops(cfg.DK, cfg.DV)
+    achieved = flops / (mean_kernel_ms * 1e-3) / 1e12
+    peak = MATRIX_PEAK_TFLOPS[args.matmul]
+    hbm = alg_bytes / (mean_kernel_ms * 1e-3) / 1e9
+    variant = f"_{args.matmul}"
+    traffic, traffic_src = committed_traffic(name + variant, "kda_prefill")
+    log(f"[bench] traffic: {traffic} ({traffic_src})")
+    copies = None
+    if not args.no_copy_ceiling:
+        copies = copy_ceiling(alg_bytes)
+        log(f"[bench] copy ceiling (read+write, {alg_bytes / 1e9:.2f} GB): {copies}")
+    cpu = None
+    if args.cpu_budget > 0:
+        log(f"[bench] cpu_baseline: oracle for ~{args.cpu_budget:.0f} s")
+        cpu = cpu_baseline(inp, pool, args.cpu_budget, heads_per_step=4)
+        cpu["value"] = cpu["tokens_heads_per_s"]
+        cpu["unit"] = "tokens·heads/s"
+        log(f"[bench] cpu_baseline {cpu['value']} token-heads/s")
+    line = {
+        "metric": PREFILL_METRIC,
+        "value": round(tok_heads / (ms_per_step * 1e-3), 1),
+        "unit": "tokens·heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16x3" if args.matmul == "split_bf16" else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": name, "B": cfg.B, "H": cfg.H, "HV": cfg.HV, "dk": cfg.DK, "dv": cfg.DV,
+            "tokens_per_request": cfg.tokens, "total_tokens": inp.T,
+            "qkv_dtype": cfg.qkv_dtype, "state_dtype": cfg.state_dtype,
+            "state_layout": cfg.state_layout, "gate": cfg.gate_mode, "matmul": args.matmul,
+            "chunk": CHUNK, "slots": cfg.n_slots, "parallelism": "single GPU",
+        },
+        "kernel_us_mean": round(mean_kernel_ms * 1e3, 2),
+        "algorithmic_flops_per_step": flops,
+        "algorithmic_bytes_per_step": alg_bytes,
+        "hbm_GBps": round(hbm, 1),
+        "copy_kernels_GBps": copies,
+        "pct_hbm_peak": round(100.0 * hbm / HBM_PEAK_GBPS, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": traffic,
+            "kernel": "kda_prefill_chunks<%d,%d,%s q/k/v,%s state,%s,%s>" % (
+                cfg.DK, cfg.DV, cfg.qkv_dtype, cfg.state_dtype, cfg.state_layout.replace("_", ""),
+                args.matmul),
+        },
+        "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
     return 0
