@@ -71,7 +71,7 @@
 // (v_mfma_f32_16x16x4_f32): fp32 products, fp32 sums.  KDA_MATMUL_SPLIT_BF16
 // writes each fp32 operand as hi + lo, both bf16 (round to nearest even),
 // and sums the three products hi*hi + hi*lo + lo*hi on the bf16 matrix
-// instructions (16x16x32 and 16x16x16): each operand keeps 16 significant
+// instruction (16x16x32; K = 16 products zero-pad K): each operand keeps 16 significant
 // bits and the dropped lo*lo term is below 2^-16 of the product, at a third
 // of the fp32 instruction's cost per product.  (This is the classic
 // split-precision product, e.g. Henry, Tang and Heinecke, "Leveraging the
@@ -90,6 +90,8 @@ namespace kda {
 namespace {
 
 constexpr int kChunk = 16;          // tokens per chunk: one MFMA M / K tile
+constexpr int kSlabCols = 32;       // value columns per wave (two MFMA N tiles)
+constexpr int kGroupChannels = 32;  // key channels per elementwise channel group
 constexpr float kSafeSpan = 80.0f;  // largest decay span of the one-product P, R
 constexpr int kPT = kChunk + 4;     // pitch of the 16-column LDS tables
 
@@ -151,6 +153,16 @@ __device__ __forceinline__ Frag<PREC, N> make_frag(const float (&x)[N]) {
   return f;
 }
 
+// A K = 16 bf16 operand widened to the K = 32 instruction's 8 values per
+// lane, the upper four zero.  Every bf16 product here runs on the gfx950
+// K = 32 instruction: with the older K = 16 bf16 instruction, results were
+// observed to depend on the compiler's instruction schedule (wrong
+// accumulator values in some schedules, right in others), so it is not used.
+__device__ __forceinline__ bf16x8 widen(const bf16x4& x) {
+  const bf16x4 z = {};
+  return __builtin_shufflevector(x, z, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // acc += A B over the fragment's K indices.
 template <int PREC, int N>
 __device__ __forceinline__ void mma(f32x4& acc, const Frag<PREC, N>& a, const Frag<PREC, N>& b) {
@@ -162,28 +174,34 @@ __device__ __forceinline__ void mma(f32x4& acc, const Frag<PREC, N>& a, const Fr
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.lo, acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, acc, 0, 0, 0);
   } else {
-    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.lo, b.hi, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.hi, b.lo, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.hi, b.hi, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen(a.lo), widen(b.hi), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen(a.hi), widen(b.lo), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen(a.hi), widen(b.hi), acc, 0, 0, 0);
   }
 }
 
 // acc += A I_nt where I_nt is the identity restricted to value tile nt: the
-// K = 32 indices (g, j) stand for the slab's columns 8g + j, B[(g, j)][n] =
-// [8g + j == 16 nt + n].  A bf16 value is exact in the hi part alone.
-template <int PREC, bool EXACT_BF16>
-__device__ __forceinline__ void mma_identity(f32x4& acc, const float (&a)[8], int nt, int n, int g) {
-  float e[8];
+// K = 4N indices (g, j) stand for the slab's columns N g + j, B[(g, j)][n] =
+// [N g + j == 16 nt + n].  A bf16 value is exact in the hi part alone.
+template <int PREC, bool EXACT_BF16, int N>
+__device__ __forceinline__ void mma_identity(f32x4& acc, const float (&a)[N], int nt, int n, int g) {
+  float e[N];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) e[j] = 8 * g + j == 16 * nt + n ? 1.0f : 0.0f;
+  for (int j = 0; j < N; ++j) e[j] = N * g + j == 16 * nt + n ? 1.0f : 0.0f;
   if constexpr (PREC == KDA_MATMUL_F32) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], e[j], acc, 0, 0, 0);
+    for (int j = 0; j < N; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], e[j], acc, 0, 0, 0);
   } else {
-    const Frag<PREC, 8> fa = make_frag<PREC, 8>(a);
-    const Frag<PREC, 8> fe = make_frag<PREC, 8>(e);
-    if constexpr (!EXACT_BF16) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa.lo, fe.hi, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa.hi, fe.hi, acc, 0, 0, 0);
+    const Frag<PREC, N> fa = make_frag<PREC, N>(a);
+    const Frag<PREC, N> fe = make_frag<PREC, N>(e);
+    if constexpr (N == 8) {
+      if constexpr (!EXACT_BF16) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa.lo, fe.hi, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa.hi, fe.hi, acc, 0, 0, 0);
+    } else {
+      if constexpr (!EXACT_BF16)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen(fa.lo), widen(fe.hi), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen(fa.hi), widen(fe.hi), acc, 0, 0, 0);
+    }
   }
 }
 
@@ -211,9 +229,11 @@ template <int DK>
 struct RowTable<KDA_MATMUL_F32, DK> {
   static constexpr int P = DK + 4;
   float v[kChunk][P];
-  __device__ __forceinline__ void store8(int t, int d0, const float (&x)[8]) {
-    *reinterpret_cast<f32x4*>(&v[t][d0]) = f32x4{x[0], x[1], x[2], x[3]};
-    *reinterpret_cast<f32x4*>(&v[t][d0 + 4]) = f32x4{x[4], x[5], x[6], x[7]};
+  template <int N>
+  __device__ __forceinline__ void store(int t, int d0, const float (&x)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; i += 4)
+      *reinterpret_cast<f32x4*>(&v[t][d0 + i]) = f32x4{x[i], x[i + 1], x[i + 2], x[i + 3]};
   }
   __device__ __forceinline__ Frag<KDA_MATMUL_F32, 8> frag8(int row, int s, int g) const {
     const f32x4 x0 = *reinterpret_cast<const f32x4*>(&v[row][32 * s + 4 * g]);
@@ -233,10 +253,12 @@ struct RowTable<KDA_MATMUL_SPLIT_BF16, DK> {
   static constexpr int P = DK + 8;
   __bf16 hi[kChunk][P];
   __bf16 lo[kChunk][P];
-  __device__ __forceinline__ void store8(int t, int d0, const float (&x)[8]) {
-    const Frag<KDA_MATMUL_SPLIT_BF16, 8> f = make_frag<KDA_MATMUL_SPLIT_BF16, 8>(x);
-    *reinterpret_cast<bf16x8*>(&hi[t][d0]) = f.hi;
-    *reinterpret_cast<bf16x8*>(&lo[t][d0]) = f.lo;
+  template <int N>
+  __device__ __forceinline__ void store(int t, int d0, const float (&x)[N]) {
+    const Frag<KDA_MATMUL_SPLIT_BF16, N> f = make_frag<KDA_MATMUL_SPLIT_BF16, N>(x);
+    typedef typename Frag<KDA_MATMUL_SPLIT_BF16, N>::vec vec;
+    *reinterpret_cast<vec*>(&hi[t][d0]) = f.hi;
+    *reinterpret_cast<vec*>(&lo[t][d0]) = f.lo;
   }
   __device__ __forceinline__ Frag<KDA_MATMUL_SPLIT_BF16, 8> frag8(int row, int s, int g) const {
     const bf16x4 h0 = *reinterpret_cast<const bf16x4*>(&hi[row][32 * s + 4 * g]);
@@ -246,6 +268,44 @@ struct RowTable<KDA_MATMUL_SPLIT_BF16, DK> {
     Frag<KDA_MATMUL_SPLIT_BF16, 8> f;
     f.hi = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
     f.lo = __builtin_shufflevector(l0, l1, 0, 1, 2, 3, 4, 5, 6, 7);
+    return f;
+  }
+};
+
+// Kup_raw^T [channel][token] in LDS, written one value at a time by the
+// lane that owns (token, channel) and read as K = 16 fragments of four
+// consecutive tokens.  The split form packs hi (upper half) and lo (lower
+// half) of one value into a word; a fragment is reassembled with byte
+// permutes instead of being split again by every wave.
+template <int PREC, int DK>
+struct KupTable;
+
+template <int DK>
+struct KupTable<KDA_MATMUL_F32, DK> {
+  float v[DK][kPT];
+  __device__ __forceinline__ void store(int d, int t, float x) { v[d][t] = x; }
+  __device__ __forceinline__ Frag<KDA_MATMUL_F32, 4> frag4(int row, int g) const {
+    return acc_frag4<KDA_MATMUL_F32>(*reinterpret_cast<const f32x4*>(&v[row][4 * g]));
+  }
+};
+
+template <int DK>
+struct KupTable<KDA_MATMUL_SPLIT_BF16, DK> {
+  uint32_t v[DK][kPT];
+  __device__ __forceinline__ void store(int d, int t, float x) {
+    const __bf16 h = static_cast<__bf16>(x);
+    const __bf16 l = static_cast<__bf16>(x - static_cast<float>(h));
+    v[d][t] = (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h)) << 16) |
+              __builtin_bit_cast(uint16_t, l);
+  }
+  __device__ __forceinline__ Frag<KDA_MATMUL_SPLIT_BF16, 4> frag4(int row, int g) const {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(&v[row][4 * g]);
+    constexpr uint32_t kUpper = 0x07060302u, kLower = 0x05040100u;
+    const u32x2 hi = {__builtin_amdgcn_perm(w[1], w[0], kUpper), __builtin_amdgcn_perm(w[3], w[2], kUpper)};
+    const u32x2 lo = {__builtin_amdgcn_perm(w[1], w[0], kLower), __builtin_amdgcn_perm(w[3], w[2], kLower)};
+    Frag<KDA_MATMUL_SPLIT_BF16, 4> f;
+    f.hi = __builtin_bit_cast(bf16x4, hi);
+    f.lo = __builtin_bit_cast(bf16x4, lo);
     return f;
   }
 };
@@ -266,41 +326,46 @@ __device__ __forceinline__ void store_elem(void* base, int64_t off, float x) {
   else static_cast<float*>(base)[off] = x;
 }
 
-// 8 consecutive elements at a 16-byte aligned element offset, kept in their
-// storage form (bf16 pairs or fp32).
-template <bool BF16>
-struct Run8 {
-  static constexpr int W = BF16 ? 4 : 8;
+// N (4 or 8) consecutive elements at an N-element aligned offset, kept in
+// their storage form (bf16 pairs or fp32).
+template <bool BF16, int N>
+struct RunN {
+  static constexpr int W = BF16 ? N / 2 : N;
   uint32_t w[W];
-  __device__ __forceinline__ void zero() {
-#pragma unroll
-    for (int i = 0; i < W; ++i) w[i] = 0;
-  }
   __device__ __forceinline__ void load(const void* base, int64_t off) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const char*>(base) + off * (BF16 ? 2 : 4));
+    const char* b = static_cast<const char*>(base) + off * (BF16 ? 2 : 4);
+    if constexpr (W == 2) {
+      const u32x2 x = *reinterpret_cast<const u32x2*>(b);
+      w[0] = x[0];
+      w[1] = x[1];
+    } else {
+      const u32x4* p = reinterpret_cast<const u32x4*>(b);
 #pragma unroll
-    for (int i = 0; i < W / 4; ++i) {
-      const u32x4 x = p[i];
+      for (int i = 0; i < W / 4; ++i) {
+        const u32x4 x = p[i];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) w[4 * i + j] = x[j];
+        for (int j = 0; j < 4; ++j) w[4 * i + j] = x[j];
+      }
     }
   }
-  __device__ __forceinline__ void unpack(float (&x)[8]) const {
+  __device__ __forceinline__ void unpack(float (&x)[N]) const {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < N; ++i) {
       if constexpr (BF16) x[i] = i % 2 == 0 ? bf16_to_f32(w[i / 2] & 0xffffu) : __uint_as_float(w[i / 2] & 0xffff0000u);
       else x[i] = __uint_as_float(w[i]);
     }
   }
 };
 
-// 4 consecutive output values of one token.
+// 4 consecutive output values of one token (bf16: the conversion
+// instruction, round to nearest even).
 template <bool BF16>
 __device__ __forceinline__ void store4(void* base, int64_t off, const f32x4& x) {
   if constexpr (BF16) {
-    const u32x2 p = {f32_to_bf16_rne(x[0]) | (f32_to_bf16_rne(x[1]) << 16),
-                     f32_to_bf16_rne(x[2]) | (f32_to_bf16_rne(x[3]) << 16)};
-    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(base) + off) = p;
+    bf16x4 p;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = static_cast<__bf16>(x[i]);
+    *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(base) + off) = p;
   } else {
     *reinterpret_cast<f32x4*>(static_cast<float*>(base) + off) = x;
   }
@@ -338,43 +403,36 @@ __device__ __forceinline__ float cross_row_sum(float x) {
 
 template <int DK, int NW, int PREC>
 struct alignas(16) ChunkShared {
+  static constexpr int NWP = (NW + 3) / 4 * 4;   // norm partials per token, padded
   // published by every wave for its channels, read by all after the barrier
   RowTable<PREC, DK> kt;          // Kt_raw = k exp(Gamma)
   RowTable<PREC, DK> qt;          // Qt_raw = q exp(Gamma)
-  float kup[DK][kPT];             // Kup_raw^T [channel][token] = k exp(Gamma_last - Gamma)
+  KupTable<PREC, DK> kup;         // Kup_raw^T [channel][token] = k exp(Gamma_last - Gamma)
   float egl[DK];                  // exp(Gamma_last)
   float beta[kChunk];
-  float nq[kChunk][4];            // per-wave partial sums of q^2, k^2 [token][wave]
-  float nk[kChunk][4];
+  float nq[kChunk][NWP];          // per-wave partial sums of q^2, k^2 [token][wave]
+  float nk[kChunk][NWP];
   float pp[NW][kChunk][kPT];      // P_raw partial of wave w, transposed: [s][t]
   float rr[NW][kChunk][kPT];      // R_raw partial of wave w: [t][s]
   // private to each wave
   float lt[NW][kChunk][kPT];      // L^T: [s][t]
   float tw[NW][kChunk][kPT];      // T = (I + L)^-1: [t][c]
-  float pq[NW][kChunk][36];       // raw q, k and Gamma of the wave's channel
-  float pk[NW][kChunk][36];       //   group, for the pair-by-pair P and R
-  float pg[NW][kChunk][36];
+  float pq[NW][kChunk][kGroupChannels + 4];   // raw q, k and Gamma of the wave's
+  float pk[NW][kChunk][kGroupChannels + 4];   //   channel group, for the pair-by-
+  float pg[NW][kChunk][kGroupChannels + 4];   //   pair P and R
 };
 
 // Raw inputs of one chunk for one lane: per channel group pass, q, k and
-// the gate pre-activation of token lane % 16 at 8 channels; the value slab's
-// 8 columns and the beta logit of that token.
+// the gate pre-activation of token lane % 16 at a quarter of the group's
+// channels; a quarter of the value slab's columns and the beta logit of that
+// token.
 template <int NP, bool QBF16>
 struct ChunkInputs {
-  Run8<QBF16> q[NP], k[NP];
-  Run8<false> x[NP];
-  Run8<QBF16> v;
+  static constexpr int CPL = kGroupChannels / 4;
+  RunN<QBF16, CPL> q[NP], k[NP];
+  RunN<false, CPL> x[NP];
+  RunN<QBF16, kSlabCols / 4> v;
   float bl;
-  __device__ __forceinline__ void zero() {
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      q[p].zero();
-      k[p].zero();
-      x[p].zero();
-    }
-    v.zero();
-    bl = 0.0f;
-  }
 };
 
 // ---------------------------------------------------------------------------
@@ -382,10 +440,15 @@ struct ChunkInputs {
 // ---------------------------------------------------------------------------
 
 template <int DK, int DV, bool QBF16, bool SBF16, bool VFIRST, int PREC>
-__global__ void __launch_bounds__(DV / 32 * kWave)
+__global__ void __launch_bounds__(DV / kSlabCols * kWave)
 kda_prefill_chunks(DecodeArgs a) {
-  constexpr int NW = DV / 32;            // waves: one 32-value slab each
-  constexpr int NG = DK / 32;            // channel groups of 32
+  constexpr int VC = kSlabCols;
+  constexpr int NTV = VC / 16;           // value tiles per wave
+  constexpr int VPL = VC / 4;            // value columns per lane in the V operand
+  constexpr int NW = DV / VC;            // waves: one VC-value slab each
+  constexpr int CGS = kGroupChannels;
+  constexpr int CPL = CGS / 4;           // channels per lane in the elementwise stage
+  constexpr int NG = DK / CGS;           // channel groups
   constexpr int NP = (NG + NW - 1) / NW; // channel group passes per wave
   constexpr int MT = DK / 16;            // state row tiles
   constexpr int KS = DK / 32;            // K = 32 steps over the channels
@@ -407,22 +470,22 @@ kda_prefill_chunks(DecodeArgs a) {
   t1 = t1 < t0 ? t0 : (t1 > a.T ? a.T : t1);
   if (t1 == t0) return;
   const int slot = a.state_indices[b];
-  const int vcol0 = 32 * w;
+  const int vcol0 = VC * w;
 
   if (slot < 0 || slot >= a.N) {   // skipped request: zero rows, no state access
     for (int t = t0; t < t1; ++t)
-      if (lane < 32) store_elem<QBF16>(a.out, (static_cast<int64_t>(t) * a.HV + hv) * DV + vcol0 + lane, 0.0f);
+      if (lane < VC) store_elem<QBF16>(a.out, (static_cast<int64_t>(t) * a.HV + hv) * DV + vcol0 + lane, 0.0f);
     return;
   }
 
   // ---- the state slab into the accumulators: S[mt][nt][i] is
   // S[16 mt + 4g + i][vcol0 + 16 nt + n]
-  f32x4 S[MT][2];
+  f32x4 S[MT][NTV];
   const int64_t tile = (static_cast<int64_t>(slot) * a.HV + hv) * DK * DV;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+    for (int nt = 0; nt < NTV; ++nt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int d = 16 * mt + 4 * g + i, v = vcol0 + 16 * nt + n;
@@ -431,47 +494,43 @@ kda_prefill_chunks(DecodeArgs a) {
       }
 
   // channel groups of this wave: group w + NW p covers channels
-  // [32 (w + NW p), +32); this lane's 8 start at chan0[p]
-  float dtb[NP][8];
+  // [CGS (w + NW p), +CGS); this lane's CPL start at chan0[p]
+  float dtb[NP][CPL];
   int chan0[NP];
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
     const int gi = w + NW * p;
-    chan0[p] = 32 * gi + 8 * g;
+    chan0[p] = CGS * gi + CPL * g;
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < CPL; ++j)
       dtb[p][j] = gi < NG ? a.dt_bias[static_cast<int64_t>(hv) * DK + chan0[p] + j] : 0.0f;
   }
   const float amp = exp_f(a.a_log[hv]);
 
+  // Loads are unconditional (a token past the request's end reads the
+  // request's last row and is zeroed where it is used), so the compiler can
+  // count them exactly and never waits for more than the oldest in flight.
   auto load_inputs = [&](ChunkInputs<NP, QBF16>& in, int c0) {
-    in.zero();
-    const int64_t tok = static_cast<int64_t>(c0) + n;
-    if (tok < t1) {
+    const int64_t tok = c0 + n < t1 ? c0 + n : t1 - 1;
 #pragma unroll
-      for (int p = 0; p < NP; ++p) {
-        if (w + NW * p < NG) {
-          const int64_t qk_off = (tok * a.H + h) * DK + chan0[p];
-          in.q[p].load(a.q, qk_off);
-          in.k[p].load(a.k, qk_off);
-          in.x[p].load(a.raw_gate, (tok * a.HV + hv) * DK + chan0[p]);
-        }
+    for (int p = 0; p < NP; ++p) {
+      if (NG % NW == 0 || w + NW * p < NG) {
+        const int64_t qk_off = (tok * a.H + h) * DK + chan0[p];
+        in.q[p].load(a.q, qk_off);
+        in.k[p].load(a.k, qk_off);
+        in.x[p].load(a.raw_gate, (tok * a.HV + hv) * DK + chan0[p]);
       }
-      in.v.load(a.v, (tok * a.HV + hv) * DV + vcol0 + 8 * g);
-      in.bl = a.beta_logits[tok * a.HV + hv];
     }
+    in.v.load(a.v, (tok * a.HV + hv) * DV + vcol0 + VPL * g);
+    in.bl = a.beta_logits[tok * a.HV + hv];
   };
 
-  ChunkInputs<NP, QBF16> cur;
-  load_inputs(cur, t0);
-
-  for (int c0 = t0; c0 < t1; c0 += kChunk) {
+  // One chunk: `cur` holds its inputs; the next chunk's go to `nxt` and
+  // stay in flight meanwhile.
+  auto chunk = [&](int c0, const ChunkInputs<NP, QBF16>& cur, ChunkInputs<NP, QBF16>& nxt) {
     const int m = t1 - c0 < kChunk ? t1 - c0 : kChunk;
     const bool live = n < m;
-
-    ChunkInputs<NP, QBF16> nxt;        // next chunk's inputs, in flight meanwhile
-    if (c0 + kChunk < t1) load_inputs(nxt, c0 + kChunk);
-    else nxt.zero();
+    load_inputs(nxt, c0 + kChunk);   // past the end: reloads the last row, unused
 
     // ================= stage E: this wave's channels, lane = (token n, quarter g)
     float sq = 0.0f, sk = 0.0f;
@@ -482,62 +541,74 @@ kda_prefill_chunks(DecodeArgs a) {
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
       if (w + NW * p >= NG) continue;
-      float q[8], k[8], x[8];
+      float q[CPL], k[CPL], x[CPL];
       cur.q[p].unpack(q);
       cur.k[p].unpack(k);
       cur.x[p].unpack(x);
-      float G[8], GL[8];
-      bool wide_lane = false;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < CPL; ++j) {     // padding tokens: q = k = 0
+        q[j] = live ? q[j] : 0.0f;
+        k[j] = live ? k[j] : 0.0f;
+      }
+      float G[CPL], GL[CPL];
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) {
         sq = fmaf(q[j], q[j], sq);
         sk = fmaf(k[j], k[j], sk);
-        const float xx = x[j] + dtb[p][j];
-        const float gj = a.gate_mode == KDA_GATE_SOFTPLUS ? -amp * softplus_f(xx)
-                                                          : a.lower_bound * sigmoid_f(amp * xx);
-        G[j] = row_scan(live ? gj : 0.0f);
+      }
+      if (a.gate_mode == KDA_GATE_SOFTPLUS) {     // uniform branch
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) G[j] = -amp * softplus_f(x[j] + dtb[p][j]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) G[j] = a.lower_bound * sigmoid_f(amp * (x[j] + dtb[p][j]));
+      }
+      bool wide_lane = false;
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) {
+        G[j] = row_scan(live ? G[j] : 0.0f);
         GL[j] = dpp_row<kDppRowBcast15, false>(G[j]);
         wide_lane |= -GL[j] > kSafeSpan;
       }
-      float kt[8], qt[8];
+      float kt[CPL], qt[CPL], egl[CPL];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < CPL; ++j) {
         const float eg = exp_f(G[j]);
+        egl[j] = dpp_row<kDppRowBcast15, false>(eg);   // exp(Gamma_last), from token 15
         kt[j] = k[j] * eg;
         qt[j] = q[j] * eg;
-        sh.kup[chan0[p] + j][n] = k[j] * exp_f(GL[j] - G[j]);
+        sh.kup.store(chan0[p] + j, n, k[j] * exp_f(GL[j] - G[j]));
       }
-      sh.kt.store8(n, chan0[p], kt);
-      sh.qt.store8(n, chan0[p], qt);
+      sh.kt.template store<CPL>(n, chan0[p], kt);
+      sh.qt.template store<CPL>(n, chan0[p], qt);
       if (n == 0) {
-        *reinterpret_cast<f32x4*>(&sh.egl[chan0[p]]) =
-            f32x4{exp_f(GL[0]), exp_f(GL[1]), exp_f(GL[2]), exp_f(GL[3])};
-        *reinterpret_cast<f32x4*>(&sh.egl[chan0[p] + 4]) =
-            f32x4{exp_f(GL[4]), exp_f(GL[5]), exp_f(GL[6]), exp_f(GL[7])};
+#pragma unroll
+        for (int j = 0; j < CPL; j += 4)
+          *reinterpret_cast<f32x4*>(&sh.egl[chan0[p] + j]) = f32x4{egl[j], egl[j + 1], egl[j + 2], egl[j + 3]};
       }
       if (!__any(wide_lane)) {
         // this group's P and R parts as one product each
-        float kp[8], qp[8], ks[8];
+        float kp[CPL], qp[CPL], ks[CPL];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < CPL; ++j) {
           const float ep = exp_f(G[j] - 0.5f * GL[j]);
           kp[j] = k[j] * ep;
           qp[j] = q[j] * ep;
           ks[j] = k[j] * __builtin_amdgcn_rcpf(ep);
         }
-        const Frag<PREC, 8> fkp = make_frag<PREC, 8>(kp);
-        const Frag<PREC, 8> fks = make_frag<PREC, 8>(ks);
-        const Frag<PREC, 8> fqp = make_frag<PREC, 8>(qp);
+        const Frag<PREC, CPL> fkp = make_frag<PREC, CPL>(kp);
+        const Frag<PREC, CPL> fks = make_frag<PREC, CPL>(ks);
+        const Frag<PREC, CPL> fqp = make_frag<PREC, CPL>(qp);
         mma(Pp, fkp, fks);    // P[t][s] = Kp[t] . Ks[s]
         mma(Rp, fks, fqp);    // R^T[s][t] = Ks[s] . Qp[t]
       } else {
         // pair by pair through the wave's scratch rows
-        *reinterpret_cast<f32x4*>(&sh.pq[w][n][8 * g]) = f32x4{q[0], q[1], q[2], q[3]};
-        *reinterpret_cast<f32x4*>(&sh.pq[w][n][8 * g + 4]) = f32x4{q[4], q[5], q[6], q[7]};
-        *reinterpret_cast<f32x4*>(&sh.pk[w][n][8 * g]) = f32x4{k[0], k[1], k[2], k[3]};
-        *reinterpret_cast<f32x4*>(&sh.pk[w][n][8 * g + 4]) = f32x4{k[4], k[5], k[6], k[7]};
-        *reinterpret_cast<f32x4*>(&sh.pg[w][n][8 * g]) = f32x4{G[0], G[1], G[2], G[3]};
-        *reinterpret_cast<f32x4*>(&sh.pg[w][n][8 * g + 4]) = f32x4{G[4], G[5], G[6], G[7]};
+#pragma unroll
+        for (int j = 0; j < CPL; j += 4) {
+          *reinterpret_cast<f32x4*>(&sh.pq[w][n][CPL * g + j]) = f32x4{q[j], q[j + 1], q[j + 2], q[j + 3]};
+          *reinterpret_cast<f32x4*>(&sh.pk[w][n][CPL * g + j]) = f32x4{k[j], k[j + 1], k[j + 2], k[j + 3]};
+          *reinterpret_cast<f32x4*>(&sh.pg[w][n][CPL * g + j]) = f32x4{G[j], G[j + 1], G[j + 2], G[j + 3]};
+        }
         wave_lds_order();
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -545,7 +616,7 @@ kda_prefill_chunks(DecodeArgs a) {
           const int tt = pi / kChunk, ss = pi % kChunk;
           if (ss <= tt) {
             float pv = 0.0f, rv = 0.0f;
-            for (int d = 0; d < 32; d += 4) {
+            for (int d = 0; d < CGS; d += 4) {
               const f32x4 kt4 = *reinterpret_cast<const f32x4*>(&sh.pk[w][tt][d]);
               const f32x4 qt4 = *reinterpret_cast<const f32x4*>(&sh.pq[w][tt][d]);
               const f32x4 gt4 = *reinterpret_cast<const f32x4*>(&sh.pg[w][tt][d]);
@@ -596,23 +667,29 @@ kda_prefill_chunks(DecodeArgs a) {
       const f32x4 bt = *reinterpret_cast<const f32x4*>(&sh.beta[4 * g]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const f32x4 pk4 = *reinterpret_cast<const f32x4*>(&sh.nk[4 * g + i][0]);
         float s2 = 0.0f;
 #pragma unroll
-        for (int ww = 0; ww < NW; ++ww) s2 += pk4[ww];
+        for (int w4 = 0; w4 < NW; w4 += 4) {
+          const f32x4 pk4 = *reinterpret_cast<const f32x4*>(&sh.nk[4 * g + i][w4]);
+#pragma unroll
+          for (int ww = 0; ww < 4 && w4 + ww < NW; ++ww) s2 += pk4[ww];
+        }
         rk[i] = rsqrt_f(s2 + a.l2_eps);
         br[i] = bt[i] * rk[i];
       }
     }
     float rkn, rqn;
     {
-      const f32x4 pk4 = *reinterpret_cast<const f32x4*>(&sh.nk[n][0]);
-      const f32x4 pq4 = *reinterpret_cast<const f32x4*>(&sh.nq[n][0]);
       float s2k = 0.0f, s2q = 0.0f;
 #pragma unroll
-      for (int ww = 0; ww < NW; ++ww) {
-        s2k += pk4[ww];
-        s2q += pq4[ww];
+      for (int w4 = 0; w4 < NW; w4 += 4) {
+        const f32x4 pk4 = *reinterpret_cast<const f32x4*>(&sh.nk[n][w4]);
+        const f32x4 pq4 = *reinterpret_cast<const f32x4*>(&sh.nq[n][w4]);
+#pragma unroll
+        for (int ww = 0; ww < 4 && w4 + ww < NW; ++ww) {
+          s2k += pk4[ww];
+          s2q += pq4[ww];
+        }
       }
       rkn = rsqrt_f(s2k + a.l2_eps);
       rqn = a.scale * rsqrt_f(s2q + a.l2_eps);
@@ -661,28 +738,30 @@ kda_prefill_chunks(DecodeArgs a) {
     }
 
     // X = V - diag(rk) Kt_raw S,  Y^T = S^T Qt_raw^T   (per value tile nt)
-    f32x4 X[2], YT[2];
+    f32x4 X[NTV], YT[NTV];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) X[nt] = YT[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int nt = 0; nt < NTV; ++nt) X[nt] = YT[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const Frag<PREC, 8> fk = sh.kt.frag8(n, s, g);
       const Frag<PREC, 8> fq = sh.qt.frag8(n, s, g);
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
+      for (int nt = 0; nt < NTV; ++nt) {
         const Frag<PREC, 8> fs = acc_frag8<PREC>(S[2 * s][nt], S[2 * s + 1][nt]);
         mma(X[nt], fk, fs);
         mma(YT[nt], fs, fq);
       }
     }
     {
-      float vv[8];
+      float vv[VPL];
       cur.v.unpack(vv);
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
+      for (int j = 0; j < VPL; ++j) vv[j] = live ? vv[j] : 0.0f;
+#pragma unroll
+      for (int nt = 0; nt < NTV; ++nt) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) X[nt][i] *= -rk[i];
-        mma_identity<PREC, QBF16>(X[nt], vv, nt, n, g);
+        mma_identity<PREC, QBF16, VPL>(X[nt], vv, nt, n, g);
       }
     }
     wave_lds_order();
@@ -691,38 +770,51 @@ kda_prefill_chunks(DecodeArgs a) {
     // S = diag(exp(Gamma_last)) S + Kup_raw^T U'
     const f32x4 t4 = *reinterpret_cast<const f32x4*>(&sh.tw[w][n][4 * g]);
     const Frag<PREC, 4> ft = acc_frag4<PREC>(t4);
+    Frag<PREC, 4> fu[NTV];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < NTV; ++nt) {
       f32x4 U = {0.0f, 0.0f, 0.0f, 0.0f};
       mma(U, ft, acc_frag4<PREC>(X[nt]));
 #pragma unroll
       for (int i = 0; i < 4; ++i) U[i] *= br[i];
-      const Frag<PREC, 4> fu = acc_frag4<PREC>(U);
+      fu[nt] = acc_frag4<PREC>(U);
       f32x4 OT = YT[nt];
-      mma(OT, fu, fr);
+      mma(OT, fu[nt], fr);
       if (live) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) OT[i] *= rqn;
         store4<QBF16>(a.out, (static_cast<int64_t>(c0 + n) * a.HV + hv) * DV + vcol0 + 16 * nt + 4 * g, OT);
       }
+    }
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const f32x4 e = *reinterpret_cast<const f32x4*>(&sh.egl[16 * mt + 4 * g]);
+    for (int mt = 0; mt < MT; ++mt) {
+      const f32x4 e = *reinterpret_cast<const f32x4*>(&sh.egl[16 * mt + 4 * g]);
+      const Frag<PREC, 4> fk = sh.kup.frag4(16 * mt + n, g);
+#pragma unroll
+      for (int nt = 0; nt < NTV; ++nt) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) S[mt][nt][i] *= e[i];
-        const f32x4 k4 = *reinterpret_cast<const f32x4*>(&sh.kup[16 * mt + n][4 * g]);
-        mma(S[mt][nt], acc_frag4<PREC>(k4), fu);
+        mma(S[mt][nt], fk, fu[nt]);
       }
     }
     lds_barrier();   // the shared tables are rewritten by the next chunk
-    cur = nxt;
+  };
+
+  ChunkInputs<NP, QBF16> in_a, in_b;
+  load_inputs(in_a, t0);
+  // every load so far (state, first inputs) completes here, outside the
+  // loop, so the loop's waits only cover the prefetch of the chunk before
+  __builtin_amdgcn_s_waitcnt(0);
+  for (int c0 = t0; c0 < t1; c0 += 2 * kChunk) {   // ping-pong between the two buffers
+    chunk(c0, in_a, in_b);
+    if (c0 + kChunk < t1) chunk(c0 + kChunk, in_b, in_a);
   }
 
   // ---- the advanced state back to its slot
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+    for (int nt = 0; nt < NTV; ++nt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int d = 16 * mt + 4 * g + i, v = vcol0 + 16 * nt + n;
@@ -739,7 +831,7 @@ template <int DK, int DV, bool QBF16, bool SBF16, bool VFIRST, int PREC>
 int launch_one(const DecodeArgs& a, hipStream_t stream) {
   const int64_t grid = static_cast<int64_t>(a.B) * a.HV;
   hipLaunchKernelGGL((kda_prefill_chunks<DK, DV, QBF16, SBF16, VFIRST, PREC>),
-                     dim3(static_cast<uint32_t>(grid)), dim3(DV / 32 * kWave), 0, stream, a);
+                     dim3(static_cast<uint32_t>(grid)), dim3(DV / kSlabCols * kWave), 0, stream, a);
   return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
