@@ -101,3 +101,97 @@ def test_prefill_matches_decode_on_one_token_requests(torch_cuda):
     _, out_d, pool_d = H.parity_case(inp, entry="decode")
     diff = float((pool_p - pool_d).abs().max()) / float(pool_d.abs().max())
     assert diff < 3e-5, diff
+
+
+@pytest.mark.parametrize("matmul", MATMULS)
+def test_prefill_custom_scale_and_eps(torch_cuda, matmul):
+    cfg = work("scale_eps", B=3, H_=2, HV=2, DK=64, DV=64, tokens="u:10..50", seed=11, qkv="f32")
+    _say("prefill scale/eps", matmul, cfg)
+    over = {"scale": 0.3, "l2_eps": 1e-3}
+    stats, _, _ = H.parity_case(wl.draw(cfg), entry="prefill", matmul=matmul, mode_overrides=over,
+                                oracle_mode=over)
+    print("scale/eps", matmul, stats, flush=True)
+
+
+def test_prefill_varlen_gqa_batch(torch_cuda):
+    """16 requests of 1..300 tokens, 8 key heads shared by 16 value heads,
+    dk = dv = 128, key-first pool; 24 sampled tiles."""
+    cfg = wl.Workload(name="prefill_varlen_gqa", B=16, H=8, HV=16, DK=128, DV=128, n_slots=40,
+                      tokens="u:1..300", gate_mode=wl.LOWER_BOUND, lower_bound=-5.0, seed=12)
+    _say("prefill varlen gqa", cfg)
+    stats, _, _ = H.parity_case(wl.draw(cfg), entry="prefill", sample=24)
+    print("varlen gqa", stats, flush=True)
+
+
+def test_prefill_deterministic_bitwise(torch_cuda):
+    torch = torch_cuda
+    cfg = work("det", B=4, H_=2, HV=4, DK=128, DV=128, tokens="u:20..70", seed=13,
+               state_layout="v_first")
+    _say("prefill determinism", cfg)
+    inp = wl.draw(cfg)
+    dev = wl.to_device(inp)
+    p1 = wl.device_pool(inp)
+    p2 = p1.clone()
+    o1 = H.run_gpu(inp, dev, p1, entry="prefill")
+    o2 = H.run_gpu(inp, dev, p2, entry="prefill")
+    torch.cuda.synchronize()
+    assert torch.equal(p1, p2)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+@pytest.mark.parametrize("layout", ["v_first", "k_first"])
+def test_prefill_then_decode_continues_the_sequence(torch_cuda, layout):
+    """The model's use: a whole prompt through kda_prefill, then single
+    tokens through kda_decode on the same slots.  The result equals the
+    oracle's token loop over the whole sequence."""
+    torch = torch_cuda
+    from gated_delta_rule_82_amd import kda
+    from oracle import kda_oracle as ko
+    n_pre, n_dec, B = 45, 3, 3
+    cfg = work("pre_dec", B=B, H_=2, HV=4, DK=128, DV=128, tokens=str(n_pre + n_dec), seed=14,
+               state_layout=layout)
+    _say("prefill then decode", layout, cfg)
+    inp = wl.draw(cfg)
+    dev = wl.to_device(inp)
+    pool = wl.device_pool(inp)
+    valid = [(b, hv) for b in range(B) for hv in range(cfg.HV)]
+    init = H.gather_tiles(pool, [int(inp.state_indices[b]) for b, _ in valid], [hv for _, hv in valid])
+    n = n_pre + n_dec
+    mode = dict(gate_mode=cfg.gate_mode, lower_bound=cfg.lower_bound, state_layout=layout)
+
+    def rows(sel):
+        idx = torch.as_tensor(np.concatenate([b * n + np.asarray(sel) for b in range(B)]),
+                              device=pool.device)
+        part = dict(dev)
+        for key in ("q", "k", "v", "raw_gate", "beta_logits"):
+            part[key] = dev[key][:, idx].contiguous()
+        return part
+
+    pre = rows(np.arange(n_pre))
+    pre["cu_seqlens"] = torch.arange(0, B * n_pre + 1, n_pre, dtype=torch.int32, device=pool.device)
+    out_pre = torch.empty((1, B * n_pre, cfg.HV, cfg.DV), dtype=torch.bfloat16, device=pool.device)
+    kda.prefill(out_pre, pre["q"], pre["k"], pre["v"], pre["raw_gate"], pre["beta_logits"],
+                pre["a_log"], pre["dt_bias"], pre["cu_seqlens"], pool, pre["state_indices"], **mode)
+    outs_dec = []
+    for t in range(n_dec):
+        one = rows([n_pre + t])
+        one["cu_seqlens"] = torch.arange(B + 1, dtype=torch.int32, device=pool.device)
+        o = torch.empty((1, B, cfg.HV, cfg.DV), dtype=torch.bfloat16, device=pool.device)
+        kda.decode(o, one["q"], one["k"], one["v"], one["raw_gate"], one["beta_logits"], one["a_log"],
+                   one["dt_bias"], one["cu_seqlens"], pool, one["state_indices"], **mode)
+        outs_dec.append(o)
+    torch.cuda.synchronize()
+
+    out = np.zeros((1, B * n, cfg.HV, cfg.DV))
+    op = H.out_to_f64(out_pre)
+    for b in range(B):
+        out[0, b * n:b * n + n_pre] = op[0, b * n_pre:(b + 1) * n_pre]
+        for t in range(n_dec):
+            out[0, b * n + n_pre + t] = H.out_to_f64(outs_dec[t])[0, b]
+    after = H.gather_tiles(pool, [int(inp.state_indices[b]) for b, _ in valid], [hv for _, hv in valid])
+    out_ref, pool_ref = H.oracle_tiles(inp, valid, init)
+    stats = H.compare_outputs(inp, valid, out, out_ref, **{k: H.PREFILL_TOL["split_bf16"][k]
+                                                           for k in ("out_floor", "out_f32_rel")})
+    stats.update(H.compare_states(after, [pool_ref[(int(inp.state_indices[b]), hv)] for b, hv in valid],
+                                  "f32", H.PREFILL_TOL["split_bf16"]["state_tight"]))
+    print("prefill then decode", layout, stats, flush=True)
