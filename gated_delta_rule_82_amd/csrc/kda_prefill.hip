@@ -525,12 +525,27 @@ kda_prefill_chunks(DecodeArgs a) {
     in.bl = a.beta_logits[tok * a.HV + hv];
   };
 
-  // One chunk: `cur` holds its inputs; the next chunk's go to `nxt` and
-  // stay in flight meanwhile.
-  auto chunk = [&](int c0, const ChunkInputs<NP, QBF16>& cur, ChunkInputs<NP, QBF16>& nxt) {
+  // One input buffer: each chunk first takes its inputs out of it (q, k
+  // and the gate unpacked, v and beta kept), then refills it with the next
+  // chunk's, which stay in flight while this chunk is processed.
+  ChunkInputs<NP, QBF16> in;
+  load_inputs(in, t0);
+  // every load so far (state, first inputs) completes here, outside the
+  // loop, so the loop's waits only cover the previous chunk's prefetch
+  __builtin_amdgcn_s_waitcnt(0);
+  for (int c0 = t0; c0 < t1; c0 += kChunk) {
     const int m = t1 - c0 < kChunk ? t1 - c0 : kChunk;
     const bool live = n < m;
-    load_inputs(nxt, c0 + kChunk);   // past the end: reloads the last row, unused
+    float qin[NP][CPL], kin[NP][CPL], xin[NP][CPL];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      in.q[p].unpack(qin[p]);
+      in.k[p].unpack(kin[p]);
+      in.x[p].unpack(xin[p]);
+    }
+    const RunN<QBF16, VPL> v_cur = in.v;
+    const float bl_cur = in.bl;
+    load_inputs(in, c0 + kChunk);   // past the end: reloads the last row, unused
 
     // ================= stage E: this wave's channels, lane = (token n, quarter g)
     float sq = 0.0f, sk = 0.0f;
@@ -542,13 +557,11 @@ kda_prefill_chunks(DecodeArgs a) {
     for (int p = 0; p < NP; ++p) {
       if (w + NW * p >= NG) continue;
       float q[CPL], k[CPL], x[CPL];
-      cur.q[p].unpack(q);
-      cur.k[p].unpack(k);
-      cur.x[p].unpack(x);
 #pragma unroll
       for (int j = 0; j < CPL; ++j) {     // padding tokens: q = k = 0
-        q[j] = live ? q[j] : 0.0f;
-        k[j] = live ? k[j] : 0.0f;
+        q[j] = live ? qin[p][j] : 0.0f;
+        k[j] = live ? kin[p][j] : 0.0f;
+        x[j] = xin[p][j];
       }
       float G[CPL], GL[CPL];
 #pragma unroll
@@ -643,7 +656,7 @@ kda_prefill_chunks(DecodeArgs a) {
     if (g == 0) {
       sh.nq[n][w] = sq;
       sh.nk[n][w] = sk;
-      if (w == 0) sh.beta[n] = live ? sigmoid_f(cur.bl) : 0.0f;
+      if (w == 0) sh.beta[n] = live ? sigmoid_f(bl_cur) : 0.0f;
     }
     *reinterpret_cast<f32x4*>(&sh.pp[w][n][4 * g]) = Pp;   // pp[s = n][t = 4g + i]
     *reinterpret_cast<f32x4*>(&sh.rr[w][n][4 * g]) = Rp;   // rr[t = n][s = 4g + i]
@@ -754,7 +767,7 @@ kda_prefill_chunks(DecodeArgs a) {
     }
     {
       float vv[VPL];
-      cur.v.unpack(vv);
+      v_cur.unpack(vv);
 #pragma unroll
       for (int j = 0; j < VPL; ++j) vv[j] = live ? vv[j] : 0.0f;
 #pragma unroll
@@ -798,16 +811,6 @@ kda_prefill_chunks(DecodeArgs a) {
       }
     }
     lds_barrier();   // the shared tables are rewritten by the next chunk
-  };
-
-  ChunkInputs<NP, QBF16> in_a, in_b;
-  load_inputs(in_a, t0);
-  // every load so far (state, first inputs) completes here, outside the
-  // loop, so the loop's waits only cover the prefetch of the chunk before
-  __builtin_amdgcn_s_waitcnt(0);
-  for (int c0 = t0; c0 < t1; c0 += 2 * kChunk) {   // ping-pong between the two buffers
-    chunk(c0, in_a, in_b);
-    if (c0 + kChunk < t1) chunk(c0 + kChunk, in_b, in_a);
   }
 
   // ---- the advanced state back to its slot
