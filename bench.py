@@ -59,10 +59,15 @@ def log(*a):
 
 
 def kernel_source_hash(op: str = "kda_decode") -> str:
+    """Hash of the kernel's sources and of the compiler flags only that file
+    gets (a counter summary is stale once either changes)."""
+    from gated_delta_rule_82_amd.build import EXTRA_FLAGS
     h = hashlib.sha256()
     for path in KERNEL_SOURCES[op]:
         with open(path, "rb") as f:
             h.update(f.read())
+    if op in EXTRA_FLAGS:
+        h.update(repr(EXTRA_FLAGS[op]).encode())
     return h.hexdigest()[:16]
 
 

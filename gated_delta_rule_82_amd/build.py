@@ -30,6 +30,13 @@ HIP_FLAGS = [
 ]
 
 
+# Per-file additions.  The prefill kernel keeps its MFMA accumulators (the
+# state slab and the chunk products) in the architectural VGPRs: its
+# elementwise work reads and scales them every chunk, and with accumulators
+# in AGPRs every such access costs a copy (measured 5-8% faster this way).
+EXTRA_FLAGS = {"kda_prefill": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _hipcc() -> str:
     for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
@@ -78,7 +85,7 @@ def build(verbose: bool = True) -> str:
     _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", f"-I{INCLUDE}", f"-I{CSRC}",
           "-c", os.path.join(CSRC, "kda_api.cpp"), "-o", api_o], verbose)
     # the kernel files compile in parallel (each takes tens of seconds)
-    cmds = [[hipcc, *HIP_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", "-c",
+    cmds = [[hipcc, *HIP_FLAGS, *EXTRA_FLAGS.get(name, []), f"-I{INCLUDE}", f"-I{CSRC}", "-c",
              os.path.join(CSRC, f"{name}.hip"), "-o", obj] for name, obj in zip(kernels, objs)]
     _run_all(cmds, verbose)
     tmp = LIB + ".tmp"
