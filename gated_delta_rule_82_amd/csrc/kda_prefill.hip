@@ -439,8 +439,15 @@ struct ChunkInputs {
 // the kernel
 // ---------------------------------------------------------------------------
 
+// At dv = 128, two workgroups per CU (256 registers per lane, two 76 KiB
+// LDS footprints in 160 KiB): the chunk step is VALU- and latency-bound at
+// one wave per SIMD, and a second workgroup's waves fill the gaps.  The
+// register cap spills only the state tile's addresses (kept from the load
+// to the final store) and two scalars per chunk.
+constexpr int prefill_blocks_per_cu(int dv) { return dv == 128 ? 2 : 1; }
+
 template <int DK, int DV, bool QBF16, bool SBF16, bool VFIRST, int PREC>
-__global__ void __launch_bounds__(DV / kSlabCols * kWave)
+__global__ void __launch_bounds__(DV / kSlabCols * kWave, prefill_blocks_per_cu(DV))
 kda_prefill_chunks(DecodeArgs a) {
   constexpr int VC = kSlabCols;
   constexpr int NTV = VC / 16;           // value tiles per wave
