@@ -136,6 +136,32 @@ struct Frag<KDA_MATMUL_SPLIT_BF16, N> {
   vec hi, lo;
 };
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Splits two fp32 values into their bf16 hi parts (one packed conversion)
+// and the bf16 lo parts of the remainders, each pair packed into a word
+// (first value in the lower half).  A remainder x - hi(x) is exact in fp32
+// (hi(x) is within a factor of two of x), so it is taken with the bf16 dot
+// product instruction straight from the packed word, x + (-1) * hi(x): one
+// instruction per value instead of widening hi(x) and subtracting.
+//
+// The selector words {-1, 0} and {0, -1} are passed through registers: the
+// compiler encodes the first as the inline constant -1.0, which the
+// instruction does not read as that bf16 pair (the remainders of first
+// values came out wrong); from a register both selectors are exact.
+__device__ __forceinline__ float minus_hi(bf16x2 h, int half, float x) {
+  uint32_t sel = half == 0 ? 0x0000bf80u : 0xbf800000u;   // bf16 -1 in the chosen half
+  asm("" : "+s"(sel));
+  return __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2, sel), x, false);
+}
+
+__device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint32_t& lo) {
+  const bf16x2 h = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+  hi = __builtin_bit_cast(uint32_t, h);
+  const bf16x2 l = {static_cast<__bf16>(minus_hi(h, 0, a)), static_cast<__bf16>(minus_hi(h, 1, b))};
+  lo = __builtin_bit_cast(uint32_t, l);
+}
+
 template <int PREC, int N>
 __device__ __forceinline__ Frag<PREC, N> make_frag(const float (&x)[N]) {
   Frag<PREC, N> f;
@@ -143,12 +169,13 @@ __device__ __forceinline__ Frag<PREC, N> make_frag(const float (&x)[N]) {
 #pragma unroll
     for (int j = 0; j < N; ++j) f.v[j] = x[j];
   } else {
+    static_assert(N % 2 == 0, "split fragments hold pairs");
+    uint32_t hi[N / 2], lo[N / 2];
 #pragma unroll
-    for (int j = 0; j < N; ++j) {
-      const __bf16 h = static_cast<__bf16>(x[j]);
-      f.hi[j] = h;
-      f.lo[j] = static_cast<__bf16>(x[j] - static_cast<float>(h));
-    }
+    for (int j = 0; j < N / 2; ++j) split_pair(x[2 * j], x[2 * j + 1], hi[j], lo[j]);
+    typedef typename Frag<PREC, N>::vec vec;
+    f.hi = __builtin_bit_cast(vec, hi);
+    f.lo = __builtin_bit_cast(vec, lo);
   }
   return f;
 }
@@ -293,10 +320,9 @@ template <int DK>
 struct KupTable<KDA_MATMUL_SPLIT_BF16, DK> {
   uint32_t v[DK][kPT];
   __device__ __forceinline__ void store(int d, int t, float x) {
-    const __bf16 h = static_cast<__bf16>(x);
-    const __bf16 l = static_cast<__bf16>(x - static_cast<float>(h));
-    v[d][t] = (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h)) << 16) |
-              __builtin_bit_cast(uint16_t, l);
+    const bf16x2 h = {static_cast<__bf16>(x), static_cast<__bf16>(x)};
+    const bf16x2 w = {static_cast<__bf16>(minus_hi(h, 1, x)), h[1]};
+    v[d][t] = __builtin_bit_cast(uint32_t, w);
   }
   __device__ __forceinline__ Frag<KDA_MATMUL_SPLIT_BF16, 4> frag4(int row, int g) const {
     const u32x4 w = *reinterpret_cast<const u32x4*>(&v[row][4 * g]);
@@ -380,7 +406,8 @@ constexpr int kDppRowShr1 = 0x111;
 constexpr int kDppRowShr2 = 0x112;
 constexpr int kDppRowShr4 = 0x114;
 constexpr int kDppRowShr8 = 0x118;
-constexpr int kDppRowBcast15 = 0x15F;   // row_newbcast:15, lane 15 of the row to all
+constexpr int kDppRowBcast0 = 0x150;    // row_newbcast:s = 0x150 + s, lane s of the row to all
+constexpr int kDppRowBcast15 = 0x15F;
 
 // inclusive prefix sum over the 16 lanes of each row
 __device__ __forceinline__ float row_scan(float x) {
@@ -395,6 +422,17 @@ __device__ __forceinline__ float row_scan(float x) {
 __device__ __forceinline__ float cross_row_sum(float x) {
   x = swap16_add(x, x);
   return swap32_add(x, x);
+}
+
+// Steps S.. of the row substitution for T = (I + L)^-1: lane (t, g) holds
+// T[t][4g + j] in t4 and -L[t][s] in nlt[s].  Row 15 updates nothing.
+template <int S>
+__device__ __forceinline__ void solve_rows(f32x4& t4, const float (&nlt)[kChunk]) {
+  if constexpr (S < kChunk - 1) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) t4[j] = fmaf(nlt[S], dpp_row<kDppRowBcast0 + S, true>(t4[j]), t4[j]);
+    solve_rows<S + 1>(t4, nlt);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -415,8 +453,7 @@ struct alignas(16) ChunkShared {
   float pp[NW][kChunk][kPT];      // P_raw partial of wave w, transposed: [s][t]
   float rr[NW][kChunk][kPT];      // R_raw partial of wave w: [t][s]
   // private to each wave
-  float lt[NW][kChunk][kPT];      // L^T: [s][t]
-  float tw[NW][kChunk][kPT];      // T = (I + L)^-1: [t][c]
+  float nl[NW][kChunk][kPT];      // -L: [t][s]
   float pq[NW][kChunk][kGroupChannels + 4];   // raw q, k and Gamma of the wave's
   float pk[NW][kChunk][kGroupChannels + 4];   //   channel group, for the pair-by-
   float pg[NW][kChunk][kGroupChannels + 4];   //   pair P and R
@@ -714,36 +751,33 @@ kda_prefill_chunks(DecodeArgs a) {
       rkn = rsqrt_f(s2k + a.l2_eps);
       rqn = a.scale * rsqrt_f(s2q + a.l2_eps);
     }
-    // L[t][s] for rows t = 4g + i, column s = n, stored transposed
+    // -L[t][s] for rows t = 4g + i, column s = n, into the wave's copy
     {
       f32x4 Pf = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int ww = 0; ww < NW; ++ww) Pf += *reinterpret_cast<const f32x4*>(&sh.pp[ww][n][4 * g]);
       const float cs = rkn * sh.beta[n];
-      f32x4 Lv;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Lv[i] = n < 4 * g + i ? rk[i] * cs * Pf[i] : 0.0f;
-      *reinterpret_cast<f32x4*>(&sh.lt[w][n][4 * g]) = Lv;
+      for (int i = 0; i < 4; ++i) sh.nl[w][4 * g + i][n] = n < 4 * g + i ? -(rk[i] * cs * Pf[i]) : 0.0f;
     }
     wave_lds_order();
-    // T = (I + L)^-1, column c = n: right-looking substitution (the rows'
-    // updates are independent, so only one multiply-add per row is serial)
+    // T = (I + L)^-1 with lane (t = n, g) holding T[t][4g + j], the A operand
+    // of T X: forward substitution over the rows, T[t][.] -= L[t][s] T[s][.]
+    // for s = 0, 1, ...; row s is final at step s and reaches every lane of
+    // its 16-lane row by DPP broadcast.  L is zero on and above the
+    // diagonal, so the update leaves rows t <= s unchanged.
+    f32x4 t4;
     {
-      float xs[kChunk];
+      float nlt[kChunk];
 #pragma unroll
-      for (int t = 0; t < kChunk; ++t) xs[t] = t == n ? 1.0f : 0.0f;
+      for (int q4 = 0; q4 < kChunk / 4; ++q4) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sh.nl[w][n][4 * q4]);
 #pragma unroll
-      for (int s = 0; s < kChunk; ++s) {
-        if (g == 0) sh.tw[w][s][n] = xs[s];
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          if (4 * q4 + 3 <= s) continue;
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sh.lt[w][s][4 * q4]);
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (4 * q4 + j > s) xs[4 * q4 + j] = fmaf(-l4[j], xs[s], xs[4 * q4 + j]);
-        }
+        for (int j = 0; j < 4; ++j) nlt[4 * q4 + j] = l4[j];
       }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) t4[j] = n == 4 * g + j ? 1.0f : 0.0f;
+      solve_rows<0>(t4, nlt);
     }
     // R_raw as the B operand of R_raw^T: lane (t = n, g) holds R[t][4g + j]
     Frag<PREC, 4> fr;
@@ -784,11 +818,9 @@ kda_prefill_chunks(DecodeArgs a) {
         mma_identity<PREC, QBF16, VPL>(X[nt], vv, nt, n, g);
       }
     }
-    wave_lds_order();
 
     // U = T X, U' = diag(beta rk) U, O^T = diag(rq)(Y^T + U'^T R_raw^T),
     // S = diag(exp(Gamma_last)) S + Kup_raw^T U'
-    const f32x4 t4 = *reinterpret_cast<const f32x4*>(&sh.tw[w][n][4 * g]);
     const Frag<PREC, 4> ft = acc_frag4<PREC>(t4);
     Frag<PREC, 4> fu[NTV];
 #pragma unroll
