@@ -141,12 +141,13 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // Splits two fp32 values into their bf16 hi parts (one packed conversion)
 // and the bf16 lo parts of the remainders, each pair packed into a word
 // (first value in the lower half).  A remainder x - hi(x) is exact in fp32
-// (hi(x) is within a factor of two of x), so it is taken with the bf16 dot
-// product instruction straight from the packed word, x + (-1) * hi(x): one
-// instruction per value instead of widening hi(x) and subtracting.
+// (hi(x) is within a factor of two of x).
 //
-// The selector words {-1, 0} and {0, -1} are passed through registers: the
-// compiler encodes the first as the inline constant -1.0, which the
+// Values that die at the split take the remainder with the bf16 dot product
+// instruction straight from the packed word, x + (-1) * hi(x): the builtin
+// selects the form that accumulates into x's register, one instruction per
+// value.  The selector words {-1, 0} and {0, -1} are passed through SGPRs:
+// the compiler encodes the first as the inline constant -1.0, which the
 // instruction does not read as that bf16 pair (the remainders of first
 // values came out wrong); from a register both selectors are exact.
 __device__ __forceinline__ float minus_hi(bf16x2 h, int half, float x) {
@@ -162,7 +163,22 @@ __device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint3
   lo = __builtin_bit_cast(uint32_t, l);
 }
 
-template <int PREC, int N>
+// The same split for values that stay live (the state): the accumulating
+// dot product would need a copy of each, so hi(x) is widened from the packed
+// word with a shift or a mask and subtracted into a new register.  The word
+// is made opaque to the compiler, which otherwise converts the first value
+// again to widen it.
+__device__ __forceinline__ void split_pair_keep(float a, float b, uint32_t& hi, uint32_t& lo) {
+  const bf16x2 h = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+  hi = __builtin_bit_cast(uint32_t, h);
+  asm("" : "+v"(hi));
+  const float ha = __builtin_bit_cast(float, hi << 16);
+  const float hb = __builtin_bit_cast(float, hi & 0xffff0000u);
+  const bf16x2 l = {static_cast<__bf16>(a - ha), static_cast<__bf16>(b - hb)};
+  lo = __builtin_bit_cast(uint32_t, l);
+}
+
+template <int PREC, int N, bool KEEP = false>
 __device__ __forceinline__ Frag<PREC, N> make_frag(const float (&x)[N]) {
   Frag<PREC, N> f;
   if constexpr (PREC == KDA_MATMUL_F32) {
@@ -172,7 +188,10 @@ __device__ __forceinline__ Frag<PREC, N> make_frag(const float (&x)[N]) {
     static_assert(N % 2 == 0, "split fragments hold pairs");
     uint32_t hi[N / 2], lo[N / 2];
 #pragma unroll
-    for (int j = 0; j < N / 2; ++j) split_pair(x[2 * j], x[2 * j + 1], hi[j], lo[j]);
+    for (int j = 0; j < N / 2; ++j) {
+      if constexpr (KEEP) split_pair_keep(x[2 * j], x[2 * j + 1], hi[j], lo[j]);
+      else split_pair(x[2 * j], x[2 * j + 1], hi[j], lo[j]);
+    }
     typedef typename Frag<PREC, N>::vec vec;
     f.hi = __builtin_bit_cast(vec, hi);
     f.lo = __builtin_bit_cast(vec, lo);
@@ -190,8 +209,14 @@ __device__ __forceinline__ bf16x8 widen(const bf16x4& x) {
   return __builtin_shufflevector(x, z, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// acc += A B over the fragment's K indices.
-template <int PREC, int N>
+// acc += A B over the fragment's K indices.  A K = 16 split product runs as
+// two K = 32 instructions with no zero padding: one operand carries hi in
+// its first four K values and lo in its last four, the other carries its
+// hi part twice, then its lo part twice, so the two instructions sum
+// (a.hi + a.lo)(b.hi + b.lo), the lo * lo term included.  The duplicated
+// operand costs register copies; DUP_A picks A for it when A is the one
+// reused across calls.
+template <int PREC, int N, bool DUP_A = false>
 __device__ __forceinline__ void mma(f32x4& acc, const Frag<PREC, N>& a, const Frag<PREC, N>& b) {
   if constexpr (PREC == KDA_MATMUL_F32) {
 #pragma unroll
@@ -200,10 +225,14 @@ __device__ __forceinline__ void mma(f32x4& acc, const Frag<PREC, N>& a, const Fr
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.hi, acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.lo, acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, acc, 0, 0, 0);
+  } else if constexpr (DUP_A) {
+    const bf16x8 bc = __builtin_shufflevector(b.hi, b.lo, 0, 1, 2, 3, 4, 5, 6, 7);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_shufflevector(a.hi, a.hi, 0, 1, 2, 3, 4, 5, 6, 7), bc, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_shufflevector(a.lo, a.lo, 0, 1, 2, 3, 4, 5, 6, 7), bc, acc, 0, 0, 0);
   } else {
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen(a.lo), widen(b.hi), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen(a.hi), widen(b.lo), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen(a.hi), widen(b.hi), acc, 0, 0, 0);
+    const bf16x8 ac = __builtin_shufflevector(a.hi, a.lo, 0, 1, 2, 3, 4, 5, 6, 7);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ac, __builtin_shufflevector(b.hi, b.hi, 0, 1, 2, 3, 4, 5, 6, 7), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ac, __builtin_shufflevector(b.lo, b.lo, 0, 1, 2, 3, 4, 5, 6, 7), acc, 0, 0, 0);
   }
 }
 
@@ -232,10 +261,11 @@ __device__ __forceinline__ void mma_identity(f32x4& acc, const float (&a)[N], in
   }
 }
 
+// Two state accumulator tiles as one K = 32 operand; the state stays live.
 template <int PREC>
 __device__ __forceinline__ Frag<PREC, 8> acc_frag8(const f32x4& lo, const f32x4& hi) {
   const float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return make_frag<PREC, 8>(v);
+  return make_frag<PREC, 8, true>(v);
 }
 
 template <int PREC>
@@ -624,14 +654,14 @@ kda_prefill_chunks(DecodeArgs a) {
 #pragma unroll
       for (int j = 0; j < CPL; ++j) {
         G[j] = row_scan(live ? G[j] : 0.0f);
-        GL[j] = dpp_row<kDppRowBcast15, false>(G[j]);
+        GL[j] = dpp_row<kDppRowBcast15, true>(G[j]);
         wide_lane |= -GL[j] > kSafeSpan;
       }
       float kt[CPL], qt[CPL], egl[CPL];
 #pragma unroll
       for (int j = 0; j < CPL; ++j) {
         const float eg = exp_f(G[j]);
-        egl[j] = dpp_row<kDppRowBcast15, false>(eg);   // exp(Gamma_last), from token 15
+        egl[j] = dpp_row<kDppRowBcast15, true>(eg);   // exp(Gamma_last), from token 15
         kt[j] = k[j] * eg;
         qt[j] = q[j] * eg;
         sh.kup.store(chan0[p] + j, n, k[j] * exp_f(GL[j] - G[j]));
@@ -826,7 +856,7 @@ kda_prefill_chunks(DecodeArgs a) {
 #pragma unroll
     for (int nt = 0; nt < NTV; ++nt) {
       f32x4 U = {0.0f, 0.0f, 0.0f, 0.0f};
-      mma(U, ft, acc_frag4<PREC>(X[nt]));
+      mma<PREC, 4, true>(U, ft, acc_frag4<PREC>(X[nt]));
 #pragma unroll
       for (int i = 0; i < 4; ++i) U[i] *= br[i];
       fu[nt] = acc_frag4<PREC>(U);
