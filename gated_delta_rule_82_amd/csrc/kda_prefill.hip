@@ -93,6 +93,7 @@ constexpr int kChunk = 16;          // tokens per chunk: one MFMA M / K tile
 constexpr int kSlabCols = 32;       // value columns per wave (two MFMA N tiles)
 constexpr int kGroupChannels = 32;  // key channels per elementwise channel group
 constexpr float kSafeSpan = 80.0f;  // largest decay span of the one-product P, R
+constexpr float kLog2e = 1.44269504088896340736f;
 constexpr int kPT = kChunk + 4;     // pitch of the 16-column LDS tables
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -439,6 +440,8 @@ constexpr int kDppRowShr8 = 0x118;
 constexpr int kDppRowBcast0 = 0x150;    // row_newbcast:s = 0x150 + s, lane s of the row to all
 constexpr int kDppRowBcast15 = 0x15F;
 
+__device__ __forceinline__ float exp2_f(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // inclusive prefix sum over the 16 lanes of each row
 __device__ __forceinline__ float row_scan(float x) {
   x += dpp_row<kDppRowShr1, true>(x);
@@ -579,7 +582,11 @@ kda_prefill_chunks(DecodeArgs a) {
     for (int j = 0; j < CPL; ++j)
       dtb[p][j] = gi < NG ? a.dt_bias[static_cast<int64_t>(hv) * DK + chan0[p] + j] : 0.0f;
   }
+  // gates are carried in base-2 units, G2 = G log2(e), so that every
+  // exp(.) of them is one exp2 instruction
   const float amp = exp_f(a.a_log[hv]);
+  const float amp2 = amp * kLog2e;
+  const float lb2 = a.lower_bound * kLog2e;
 
   // Loads are unconditional (a token past the request's end reads the
   // request's last row and is zeroed where it is used), so the compiler can
@@ -643,28 +650,31 @@ kda_prefill_chunks(DecodeArgs a) {
         sq = fmaf(q[j], q[j], sq);
         sk = fmaf(k[j], k[j], sk);
       }
+      // G, GL: Gamma and Gamma_last of the lane's channels, times log2(e)
       if (a.gate_mode == KDA_GATE_SOFTPLUS) {     // uniform branch
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) G[j] = -amp * softplus_f(x[j] + dtb[p][j]);
+        for (int j = 0; j < CPL; ++j) G[j] = -amp2 * softplus_f(x[j] + dtb[p][j]);
       } else {
+        // lb sigmoid(z) = lb / (1 + exp(-z)),  exp(-z) = exp2(-z log2(e))
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) G[j] = a.lower_bound * sigmoid_f(amp * (x[j] + dtb[p][j]));
+        for (int j = 0; j < CPL; ++j)
+          G[j] = lb2 * __builtin_amdgcn_rcpf(1.0f + exp2_f(-amp2 * (x[j] + dtb[p][j])));
       }
       bool wide_lane = false;
 #pragma unroll
       for (int j = 0; j < CPL; ++j) {
         G[j] = row_scan(live ? G[j] : 0.0f);
         GL[j] = dpp_row<kDppRowBcast15, true>(G[j]);
-        wide_lane |= -GL[j] > kSafeSpan;
+        wide_lane |= -GL[j] > kSafeSpan * kLog2e;
       }
       float kt[CPL], qt[CPL], egl[CPL];
 #pragma unroll
       for (int j = 0; j < CPL; ++j) {
-        const float eg = exp_f(G[j]);
+        const float eg = exp2_f(G[j]);
         egl[j] = dpp_row<kDppRowBcast15, true>(eg);   // exp(Gamma_last), from token 15
         kt[j] = k[j] * eg;
         qt[j] = q[j] * eg;
-        sh.kup.store(chan0[p] + j, n, k[j] * exp_f(GL[j] - G[j]));
+        sh.kup.store(chan0[p] + j, n, k[j] * exp2_f(GL[j] - G[j]));
       }
       sh.kt.template store<CPL>(n, chan0[p], kt);
       sh.qt.template store<CPL>(n, chan0[p], qt);
@@ -678,7 +688,7 @@ kda_prefill_chunks(DecodeArgs a) {
         float kp[CPL], qp[CPL], ks[CPL];
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
-          const float ep = exp_f(G[j] - 0.5f * GL[j]);
+          const float ep = exp2_f(fmaf(-0.5f, GL[j], G[j]));
           kp[j] = k[j] * ep;
           qp[j] = q[j] * ep;
           ks[j] = k[j] * __builtin_amdgcn_rcpf(ep);
@@ -711,7 +721,7 @@ kda_prefill_chunks(DecodeArgs a) {
               const f32x4 gs4 = *reinterpret_cast<const f32x4*>(&sh.pg[w][ss][d]);
 #pragma unroll
               for (int j = 0; j < 4; ++j) {
-                const float e = ks4[j] * exp_f(fminf(gt4[j] - gs4[j], 0.0f));
+                const float e = ks4[j] * exp2_f(fminf(gt4[j] - gs4[j], 0.0f));
                 pv = fmaf(kt4[j], e, pv);
                 rv = fmaf(qt4[j], e, rv);
               }
