@@ -509,11 +509,10 @@ struct ChunkInputs {
 // the kernel
 // ---------------------------------------------------------------------------
 
-// At dv = 128, two workgroups per CU (256 registers per lane, two 76 KiB
-// LDS footprints in 160 KiB): the chunk step is VALU- and latency-bound at
-// one wave per SIMD, and a second workgroup's waves fill the gaps.  The
-// register cap spills only the state tile's addresses (kept from the load
-// to the final store) and two scalars per chunk.
+// At dv = 128, two workgroups per CU (at most 256 registers per lane, two
+// 70 KiB LDS footprints in 160 KiB): the chunk step is VALU- and
+// latency-bound at one wave per SIMD, and a second workgroup's waves fill
+// the gaps.
 constexpr int prefill_blocks_per_cu(int dv) { return dv == 128 ? 2 : 1; }
 
 template <int DK, int DV, bool QBF16, bool SBF16, bool VFIRST, int PREC>
