@@ -60,23 +60,25 @@
 // Per chunk: every wave builds its channels' operands and partials and
 // publishes them in LDS (Kt, Qt, Kup^T, exp(Gamma_last), norms, P and R
 // partials); after one workgroup barrier each wave assembles L, solves
-// T = (I + L)^-1 itself (right-looking substitution, 16 lanes) and runs X,
-// Y^T, U, O^T and the state update on its slab; a second barrier frees the
-// tables for the next chunk.  The next chunk's inputs are loaded into
+// T = (I + L)^-1 itself (forward substitution over the rows, each final row
+// broadcast along the 16-lane rows by DPP) and runs X, Y^T, U, O^T and the
+// state update on its slab; a second barrier frees the tables for the next
+// chunk.  The next chunk's inputs are loaded into
 // registers while the current one is processed, and the barriers fence LDS
 // only, so those loads stay in flight.  The state makes one trip from HBM
 // and one back per request.
 //
 // Matrix precision.  KDA_MATMUL_F32 uses the fp32 matrix instruction
 // (v_mfma_f32_16x16x4_f32): fp32 products, fp32 sums.  KDA_MATMUL_SPLIT_BF16
-// writes each fp32 operand as hi + lo, both bf16 (round to nearest even),
-// and sums the three products hi*hi + hi*lo + lo*hi on the bf16 matrix
-// instruction (16x16x32; K = 16 products zero-pad K): each operand keeps 16 significant
-// bits and the dropped lo*lo term is below 2^-16 of the product, at a third
-// of the fp32 instruction's cost per product.  (This is the classic
-// split-precision product, e.g. Henry, Tang and Heinecke, "Leveraging the
-// bfloat16 artificial intelligence datatype for higher-precision
-// computations", ARITH 2019.)
+// writes each fp32 operand as hi + lo, both bf16 (round to nearest even).
+// A K = 32 product sums hi*hi + hi*lo + lo*hi on the bf16 matrix
+// instruction (16x16x32): each operand keeps 16 significant bits and the
+// dropped lo*lo term is below 2^-16 of the product, at a third of the fp32
+// instruction's cost per product.  A K = 16 product packs hi and lo along
+// K and takes two instructions, lo*lo included (see mma).  (This is the
+// classic split-precision product, e.g. Henry, Tang and Heinecke,
+// "Leveraging the bfloat16 artificial intelligence datatype for
+// higher-precision computations", ARITH 2019.)
 
 #include <hip/hip_runtime.h>
 
@@ -201,7 +203,8 @@ __device__ __forceinline__ Frag<PREC, N> make_frag(const float (&x)[N]) {
 }
 
 // A K = 16 bf16 operand widened to the K = 32 instruction's 8 values per
-// lane, the upper four zero.  Every bf16 product here runs on the gfx950
+// lane, the upper four zero (the identity product of a 16-column slab).
+// Every bf16 product here runs on the gfx950
 // K = 32 instruction: with the older K = 16 bf16 instruction, results were
 // observed to depend on the compiler's instruction schedule (wrong
 // accumulator values in some schedules, right in others), so it is not used.
