@@ -139,3 +139,40 @@ def test_strong_decay_needs_the_pairwise_form():
     np.testing.assert_allclose(o, o_ref, rtol=1e-10, atol=1e-12)
     np.testing.assert_allclose(S, S_ref, rtol=1e-10, atol=1e-300)
     assert math.isfinite(float(np.abs(o).max()))
+
+
+def _chunk_group_spans(inp, group=32, C=16):
+    """max_d -Gamma_last[d] of every (request, value head, chunk, channel group)
+    of a drawn workload, from the oracle's gate: the quantity the prefill
+    compares with its one-product bound, per wave's channel group."""
+    cfg = inp.cfg
+    spans = []
+    for b in range(cfg.B):
+        t0, t1 = int(inp.cu_seqlens[b]), int(inp.cu_seqlens[b + 1])
+        if int(inp.state_indices[b]) < 0:
+            continue
+        for hv in range(cfg.HV):
+            g = ko.gate(inp.raw_gate[0, t0:t1, hv], inp.dt_bias[hv], inp.a_log[hv],
+                        gate_mode=cfg.gate_mode,
+                        lower_bound=cfg.lower_bound if cfg.gate_mode == wl.LOWER_BOUND else None)
+            for c0 in range(0, t1 - t0, C):
+                last = -g[c0:c0 + C].sum(axis=0)
+                spans += [float(last[d0:d0 + group].max()) for d0 in range(0, cfg.DK, group)]
+    return np.array(spans)
+
+
+def test_prefill_gpu_cases_reach_both_p_r_forms():
+    """The GPU prefill cases with a softplus gate must contain channel groups
+    on both sides of the one-product bound (so both the factored and the
+    pair-by-pair P, R run), and the lower-bound cases (span <= 16 * 5) only
+    the factored side."""
+    from tests.test_gpu_prefill import CASES
+    wide = narrow = 0
+    for name, cfg in CASES.items():
+        spans = _chunk_group_spans(wl.draw(cfg), group=min(32, cfg.DK))
+        if cfg.gate_mode == wl.SOFTPLUS:
+            wide += int((spans > SAFE_SPAN).sum())
+            narrow += int((spans <= SAFE_SPAN).sum())
+        else:
+            assert spans.max() <= 16 * abs(cfg.lower_bound) <= SAFE_SPAN, name
+    assert wide > 0 and narrow > 0, (wide, narrow)
