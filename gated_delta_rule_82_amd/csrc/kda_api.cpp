@@ -9,6 +9,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <initializer_list>
 #include <limits>
 #include <vector>
 
@@ -19,21 +20,34 @@ namespace {
 
 bool supported_head_dim(int64_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
-int64_t numel(const kda_tensor* t) {
-  int64_t n = 1;
-  for (int i = 0; i < t->ndim; ++i) n *= t->shape[i];
-  return n;
-}
-
 // Rank and non-negative extents; a NULL data pointer only for empty tensors.
 int check_tensor(const kda_tensor* t, int ndim) {
   if (t == nullptr) return KDA_ERR_NULL;
   if (t->ndim != ndim) return KDA_ERR_SHAPE;
-  for (int i = 0; i < ndim; ++i)
+  bool empty = false;
+  for (int i = 0; i < ndim; ++i) {
     if (t->shape[i] < 0) return KDA_ERR_SHAPE;
-  if (t->data == nullptr && numel(t) > 0) return KDA_ERR_NULL;
+    empty |= t->shape[i] == 0;
+  }
+  if (t->data == nullptr && !empty) return KDA_ERR_NULL;
   return KDA_OK;
 }
+
+// Whether the product of non-negative factors exceeds `limit` (computed by
+// division, so no intermediate product can overflow).
+bool product_exceeds(std::initializer_list<int64_t> factors, int64_t limit) {
+  for (int64_t f : factors)
+    if (f == 0) return false;
+  int64_t p = 1;
+  for (int64_t f : factors) {
+    if (p > limit / f) return true;
+    p *= f;
+  }
+  return false;
+}
+
+// One dispatch covers at most this many work-items (a 32-bit count).
+constexpr int64_t kMaxWorkItems = std::numeric_limits<uint32_t>::max();
 
 bool aligned(const kda_tensor* t, uintptr_t bytes) {
   return (reinterpret_cast<uintptr_t>(t->data) % bytes) == 0;
@@ -143,7 +157,7 @@ int plan_decode(const kda_tensor* out, const kda_tensor* q, const kda_tensor* k,
   if (beta_logits->shape[2] != HV) return KDA_ERR_SHAPE;
   if (a_log->shape[0] != HV || dt_bias->shape[0] != HV || dt_bias->shape[1] != DK)
     return KDA_ERR_SHAPE;
-  if (cu_seqlens->shape[0] != B + 1) return KDA_ERR_SHAPE;
+  if (cu_seqlens->shape[0] - 1 != B) return KDA_ERR_SHAPE;
   if (mode->state_layout != KDA_STATE_K_FIRST && mode->state_layout != KDA_STATE_V_FIRST)
     return KDA_ERR_MODE;
   const bool v_first = mode->state_layout == KDA_STATE_V_FIRST;
@@ -153,9 +167,15 @@ int plan_decode(const kda_tensor* out, const kda_tensor* q, const kda_tensor* k,
   if (H < 1 || HV < 1 || HV % H != 0) return KDA_ERR_SHAPE;
 
   if (!supported_head_dim(DK) || !supported_head_dim(DV)) return KDA_ERR_UNSUPPORTED;
+  // Sizes one launch can take: T, N and B fit the kernels' 32-bit indices,
+  // and the grid fits one dispatch, whose extent is a 32-bit count of
+  // work-items: 64 per (request, value head, 32-column slab) for the decode
+  // and the prefill (the q/k convolution's grid is checked with its other
+  // arguments).
   constexpr int64_t kI32 = std::numeric_limits<int32_t>::max();
   const int64_t slabs = DV < 32 ? 1 : DV / 32;
-  if (T > kI32 || N > kI32 || B * HV * slabs > kI32) return KDA_ERR_UNSUPPORTED;
+  if (T > kI32 || N > kI32 || B > kI32 || product_exceeds({B, HV, slabs, 64}, kMaxWorkItems))
+    return KDA_ERR_UNSUPPORTED;
   // 16-byte alignment: the kernel moves the state with 128-bit accesses and
   // the token rows with 32/64-bit accesses
   const kda_tensor* all[] = {out, q, k, v, raw_gate, beta_logits, a_log, dt_bias,
@@ -265,6 +285,8 @@ int kda_decode_conv(const kda_tensor* out, const kda_conv* conv, const kda_tenso
     if (wins[s]->shape[0] != N || wins[s]->shape[1] != K - 1 || wins[s]->shape[2] != (s < 2 ? CQ : CV))
       return KDA_ERR_SHAPE;
   if (K < 2 || K > 4) return KDA_ERR_UNSUPPORTED;
+  // the q/k convolution runs 128 work-items per (request, key head)
+  if (product_exceeds({static_cast<int64_t>(d.B), H, 128}, kMaxWorkItems)) return KDA_ERR_UNSUPPORTED;
   const kda_tensor* extra[] = {&conv->x_q, &conv->x_k, &conv->w_q, &conv->w_k, &conv->w_v,
                                &conv->win_q, &conv->win_k, &conv->win_v};
   for (const kda_tensor* t : extra)

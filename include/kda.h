@@ -62,8 +62,11 @@ enum kda_status {
   KDA_ERR_NULL = -1,        /* a required pointer (struct or data) is NULL  */
   KDA_ERR_DTYPE = -2,       /* a tensor has a dtype this argument rejects   */
   KDA_ERR_SHAPE = -3,       /* ranks or extents disagree (incl. HV % H)     */
-  KDA_ERR_UNSUPPORTED = -4, /* dk or dv outside {16, 32, 64, 128}, or a    */
-                            /* mix of dtypes that has no kernel             */
+  KDA_ERR_UNSUPPORTED = -4, /* dk or dv outside {16, 32, 64, 128}, data    */
+                            /* not 16-byte aligned, or a batch too large   */
+                            /* for one launch (T, N or B above 2^31 - 1,   */
+                            /* B * HV * max(dv / 32, 1) above 2^26 - 1, or */
+                            /* for the convolution B * H above 2^25 - 1)   */
   KDA_ERR_MODE = -5,        /* bad gate mode, lower_bound, l2_eps, scale or */
                             /* state layout                                 */
   KDA_ERR_LAUNCH = -6,      /* the HIP launch itself reported an error      */

@@ -317,3 +317,30 @@ def test_prefill_shares_the_decode_checks():
     assert call_prefill(e) == kda.KDA_ERR_SHAPE
     assert call_prefill(d, gate_mode=7) == kda.KDA_ERR_MODE
     assert call_prefill(d, gate_mode="lower_bound", lower_bound=0.5) == kda.KDA_ERR_MODE
+
+
+# ---------------------------------------------------------------------------
+# sizes one launch cannot take (rejected by the checker, nothing launched)
+# ---------------------------------------------------------------------------
+
+def test_grids_beyond_one_dispatch_are_unsupported():
+    # a dispatch covers at most 2^32 - 1 work-items; decode and prefill run
+    # 64 per (request, value head, 32-column slab): 2^22 x 4 x 4 x 64 = 2^32
+    d = descriptors(B=2 ** 22, HV=4, DV=128)
+    assert call(d) == kda.KDA_ERR_UNSUPPORTED
+    assert call_prefill(d) == kda.KDA_ERR_UNSUPPORTED
+    d = descriptors(B=2 ** 24, H=2, HV=4, DV=16)          # one slab: 2^24 x 4 x 64
+    assert call(d) == kda.KDA_ERR_UNSUPPORTED
+    # the q/k convolution runs 128 per (request, key head): 2^24 x 2 x 128
+    d, conv = conv_descriptors(B=2 ** 24, H=2, HV=2, DV=16)
+    assert call_conv(d, conv) == kda.KDA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("B,T", [(2 ** 31, 3), (2 ** 62, 3), (2 ** 63 - 2, 3), (2, 2 ** 31),
+                                 (2, 2 ** 62)])
+def test_huge_extents_are_rejected_without_overflow(B, T):
+    d = descriptors(B=B, T=T)
+    assert call(d) == kda.KDA_ERR_UNSUPPORTED
+    assert call_prefill(d) == kda.KDA_ERR_UNSUPPORTED
+    d, conv = conv_descriptors(B=B, T=T)
+    assert call_conv(d, conv) == kda.KDA_ERR_UNSUPPORTED
