@@ -696,6 +696,24 @@ __global__ __launch_bounds__(kWave) void kda_decode_vfirst(const DecodeArgs a) {
 // dispatch
 // ---------------------------------------------------------------------------
 
+// Occupancy cap for single-token batches on an fp32 pool.  With one token
+// per request a wave is almost all state traffic, and at dk = dv = 128 two
+// waves per SIMD stream an fp32 pool faster than four (measured on the
+// 96-head batch: key-first 545 -> 536 us, value-first 570 -> 549 us; the
+// 32-head batch key-first 55.7 -> 52.6 us).  Multi-token batches and bf16
+// pools lose with the cap, and so does a value-first batch of fewer than
+// kCapMinWaves waves (the 32-head batch, 52.1 -> 54.5 us): those keep the
+// full occupancy.  The cap is taken through dynamic LDS that the kernel
+// never touches: at kCappedLds bytes per one-wave workgroup, eight
+// workgroups fill a CU's 160 KiB, two waves per SIMD.
+constexpr size_t kCappedLds = 18560;
+constexpr int64_t kCapMinWaves = 16384;   // four rounds at four waves per SIMD
+
+template <int DK, int DV>
+constexpr size_t static_lds() {   // the kernels' tables: red_tab, upd_tab, u_tab
+  return 2 * 2 * DK * sizeof(float2) + (DV < 32 ? DV : 32) * sizeof(float);
+}
+
 template <int DK, int DV, bool QBF16, bool SBF16, int LAYOUT, bool CONVV>
 hipError_t launch_one(const DecodeArgs& args, hipStream_t stream) {
   constexpr int CW = DV < 32 ? DV : 32;
@@ -704,7 +722,11 @@ hipError_t launch_one(const DecodeArgs& args, hipStream_t stream) {
   const void* fn = LAYOUT == KDA_STATE_K_FIRST
                        ? reinterpret_cast<const void*>(&kda_decode_kfirst<DK, DV, QBF16, SBF16, CONVV>)
                        : reinterpret_cast<const void*>(&kda_decode_vfirst<DK, DV, QBF16, SBF16, CONVV>);
-  return hipLaunchKernel(fn, dim3(static_cast<uint32_t>(nwg)), dim3(kWave), kargs, 0, stream);
+  static_assert(static_lds<DK, DV>() < kCappedLds, "cap above the tables");
+  const bool cap = DK == 128 && DV == 128 && !SBF16 && args.T <= args.B &&
+                   (LAYOUT == KDA_STATE_K_FIRST || nwg >= kCapMinWaves);
+  const size_t dyn_lds = cap ? kCappedLds - static_lds<DK, DV>() : 0;
+  return hipLaunchKernel(fn, dim3(static_cast<uint32_t>(nwg)), dim3(kWave), kargs, dyn_lds, stream);
 }
 
 using LaunchFn = hipError_t (*)(const DecodeArgs&, hipStream_t);
