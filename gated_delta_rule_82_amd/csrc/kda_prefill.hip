@@ -208,7 +208,7 @@ __device__ __forceinline__ Frag<PREC, N> make_frag(const float (&x)[N]) {
 // K = 32 instruction: with the older K = 16 bf16 instruction, results were
 // observed to depend on the compiler's instruction schedule (wrong
 // accumulator values in some schedules, right in others), so it is not used.
-__device__ __forceinline__ bf16x8 widen(const bf16x4& x) {
+[[maybe_unused]] __device__ __forceinline__ bf16x8 widen(const bf16x4& x) {
   const bf16x4 z = {};
   return __builtin_shufflevector(x, z, 0, 1, 2, 3, 4, 5, 6, 7);
 }
@@ -911,12 +911,16 @@ kda_prefill_chunks(DecodeArgs a) {
 // dispatch
 // ---------------------------------------------------------------------------
 
+// The launch's own status decides KDA_ERR_LAUNCH (hipGetLastError could
+// also report an earlier, unrelated error of the calling thread).
 template <int DK, int DV, bool QBF16, bool SBF16, bool VFIRST, int PREC>
 int launch_one(const DecodeArgs& a, hipStream_t stream) {
   const int64_t grid = static_cast<int64_t>(a.B) * a.HV;
-  hipLaunchKernelGGL((kda_prefill_chunks<DK, DV, QBF16, SBF16, VFIRST, PREC>),
-                     dim3(static_cast<uint32_t>(grid)), dim3(DV / kSlabCols * kWave), 0, stream, a);
-  return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+  void* kargs[] = {const_cast<DecodeArgs*>(&a)};
+  const hipError_t rc =
+      hipLaunchKernel(reinterpret_cast<const void*>(&kda_prefill_chunks<DK, DV, QBF16, SBF16, VFIRST, PREC>),
+                      dim3(static_cast<uint32_t>(grid)), dim3(DV / kSlabCols * kWave), kargs, 0, stream);
+  return rc == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
 template <int DK, int DV, bool QBF16, bool SBF16, bool VFIRST>
