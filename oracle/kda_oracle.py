@@ -48,9 +48,11 @@ the design notes of the repository):
 
 Parity status: every function below is pinned by the CPU tests
 (``tests/test_oracle_pins.py``) against closed forms, hand-worked values,
-brute-force matrix forms and invariants, except the choice between the
-possible L2-norm epsilon placements and the lower-bound gate reading, which
-the pages do not fix (see the readings above).
+brute-force matrix forms and invariants, except two choices the pages do
+not fix: where the L2-norm epsilon goes, and the lower-bound gate reading.
+For those two the result is parity unpinned beyond the stated readings (the
+epsilon placements differ by about eps / |x|^2; the lower-bound form is
+pinned only by the three statements it is read from).
 """
 from __future__ import annotations
 
