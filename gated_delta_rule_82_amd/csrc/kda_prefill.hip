@@ -95,6 +95,17 @@ constexpr int kChunk = 16;          // tokens per chunk: one MFMA M / K tile
 constexpr int kSlabCols = 32;       // value columns per wave (two MFMA N tiles)
 constexpr int kGroupChannels = 32;  // key channels per elementwise channel group
 constexpr float kSafeSpan = 80.0f;  // largest decay span of the one-product P, R
+// Pair-by-pair exponents Gamma_t - Gamma_s are differences of prefix sums;
+// in fp32 they carry an error near ulp(|Gamma|), harmless while a chunk's
+// decay span stays within kExactSpan (in log2 units; ulp(512) = 2^-14 gives
+// factor errors of order 1e-5).  A wider span, or a non-finite one, splits
+// each token's log2-decay g into a multiple of kGateStep, whose prefix sums
+// are exact in fp32, and a remainder in (-kGateStep, 0]; g is first raised
+// to -kGateFloor (exp2 of it is already 0 in fp32), which keeps an infinite
+// decay finite: prefix sums stay below 2^24 in magnitude.
+constexpr float kExactSpan = 512.0f;
+constexpr float kGateStep = 8.0f;
+constexpr float kGateFloor = 1048576.0f;   // 2^20
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr int kPT = kChunk + 4;     // pitch of the 16-column LDS tables
 
@@ -492,7 +503,8 @@ struct alignas(16) ChunkShared {
   float nl[NW][kChunk][kPT];      // -L: [t][s]
   float pq[NW][kChunk][kGroupChannels + 4];   // raw q, k and Gamma of the wave's
   float pk[NW][kChunk][kGroupChannels + 4];   //   channel group, for the pair-by-
-  float pg[NW][kChunk][kGroupChannels + 4];   //   pair P and R
+  float pg[NW][kChunk][kGroupChannels + 4];   //   pair P and R (Gamma as its exact
+  float ps[NW][kChunk][kGroupChannels + 4];   //   multiples of 8 and remainders)
 };
 
 // Raw inputs of one chunk for one lane: per channel group pass, q, k and
@@ -511,6 +523,58 @@ struct ChunkInputs {
 // ---------------------------------------------------------------------------
 // the kernel
 // ---------------------------------------------------------------------------
+
+// Per-token log2-decays of N channels, log2(e) g: the softplus form
+// -exp(A_log) softplus(x + dt_bias), or the lower-bound form
+// lb sigmoid(exp(A_log) (x + dt_bias)) = lb / (1 + exp(-z)) with
+// exp(-z) = exp2(-z log2(e)); zero for a padding token.
+template <int N>
+__device__ __forceinline__ void log2_decays(int gate_mode, float amp2, float lb2, bool live,
+                                            const float (&x)[N], const float (&dtb)[N], float (&G)[N]) {
+  if (gate_mode == KDA_GATE_SOFTPLUS) {     // uniform branch
+#pragma unroll
+    for (int j = 0; j < N; ++j) G[j] = -amp2 * softplus_f(x[j] + dtb[j]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < N; ++j) G[j] = lb2 * __builtin_amdgcn_rcpf(1.0f + exp2_f(-amp2 * (x[j] + dtb[j])));
+  }
+#pragma unroll
+  for (int j = 0; j < N; ++j) G[j] = live ? G[j] : 0.0f;
+}
+
+// The pair-by-pair parts of P_raw and R_raw^T over one wave's channel
+// group: lane pairs (t, s), s <= t, four per lane.  The table rows hold raw
+// q and k and Gamma, the latter as one prefix sum or (EXACT) as its exact
+// multiples of kGateStep in pg and the remainders in ps.
+template <bool EXACT, class Shared>
+__device__ __forceinline__ void pair_sums(const Shared& sh, int w, int lane, float (&pw)[4], float (&rw)[4]) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int pi = lane + 64 * r;
+    const int tt = pi / kChunk, ss = pi % kChunk;
+    if (ss <= tt) {
+      float pv = 0.0f, rv = 0.0f;
+      for (int d = 0; d < kGroupChannels; d += 4) {
+        const f32x4 kt4 = *reinterpret_cast<const f32x4*>(&sh.pk[w][tt][d]);
+        const f32x4 qt4 = *reinterpret_cast<const f32x4*>(&sh.pq[w][tt][d]);
+        const f32x4 ks4 = *reinterpret_cast<const f32x4*>(&sh.pk[w][ss][d]);
+        f32x4 dg = *reinterpret_cast<const f32x4*>(&sh.pg[w][tt][d]) -
+                   *reinterpret_cast<const f32x4*>(&sh.pg[w][ss][d]);   // Gamma_t - Gamma_s
+        if constexpr (EXACT)
+          dg += *reinterpret_cast<const f32x4*>(&sh.ps[w][tt][d]) -
+                *reinterpret_cast<const f32x4*>(&sh.ps[w][ss][d]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float e = ks4[j] * exp2_f(fminf(dg[j], 0.0f));
+          pv = fmaf(kt4[j], e, pv);
+          rv = fmaf(qt4[j], e, rv);
+        }
+      }
+      pw[r] += pv;
+      rw[r] += rv;
+    }
+  }
+}
 
 // At dv = 128, two workgroups per CU (at most 256 registers per lane, two
 // 70 KiB LDS footprints in 160 KiB): the chunk step is VALU- and
@@ -653,30 +717,87 @@ kda_prefill_chunks(DecodeArgs a) {
         sk = fmaf(k[j], k[j], sk);
       }
       // G, GL: Gamma and Gamma_last of the lane's channels, times log2(e)
-      if (a.gate_mode == KDA_GATE_SOFTPLUS) {     // uniform branch
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) G[j] = -amp2 * softplus_f(x[j] + dtb[p][j]);
-      } else {
-        // lb sigmoid(z) = lb / (1 + exp(-z)),  exp(-z) = exp2(-z log2(e))
-#pragma unroll
-        for (int j = 0; j < CPL; ++j)
-          G[j] = lb2 * __builtin_amdgcn_rcpf(1.0f + exp2_f(-amp2 * (x[j] + dtb[p][j])));
-      }
+      log2_decays<CPL>(a.gate_mode, amp2, lb2, live, x, dtb[p], G);
       bool wide_lane = false;
 #pragma unroll
       for (int j = 0; j < CPL; ++j) {
-        G[j] = row_scan(live ? G[j] : 0.0f);
+        G[j] = row_scan(G[j]);
         GL[j] = dpp_row<kDppRowBcast15, true>(G[j]);
-        wide_lane |= -GL[j] > kSafeSpan * kLog2e;
+        wide_lane |= !(-GL[j] <= kSafeSpan * kLog2e);
       }
       float kt[CPL], qt[CPL], egl[CPL];
+      const bool wide = __any(wide_lane);
+      bool exact = false;
+      if (wide) {
+        bool exact_lane = false;
 #pragma unroll
-      for (int j = 0; j < CPL; ++j) {
-        const float eg = exp2_f(G[j]);
-        egl[j] = dpp_row<kDppRowBcast15, true>(eg);   // exp(Gamma_last), from token 15
-        kt[j] = k[j] * eg;
-        qt[j] = q[j] * eg;
-        sh.kup.store(chan0[p] + j, n, k[j] * exp2_f(GL[j] - G[j]));
+        for (int j = 0; j < CPL; ++j) exact_lane |= !(-GL[j] <= kExactSpan);
+        exact = __any(exact_lane);
+      }
+      if (!exact) {
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+          const float eg = exp2_f(G[j]);
+          egl[j] = dpp_row<kDppRowBcast15, true>(eg);   // exp(Gamma_last), from token 15
+          kt[j] = k[j] * eg;
+          qt[j] = q[j] * eg;
+          sh.kup.store(chan0[p] + j, n, k[j] * exp2_f(GL[j] - G[j]));
+        }
+        if (wide) {
+#pragma unroll
+          for (int j = 0; j < CPL; j += 4)
+            *reinterpret_cast<f32x4*>(&sh.pg[w][n][CPL * g + j]) = f32x4{G[j], G[j + 1], G[j + 2], G[j + 3]};
+        }
+      } else {
+        // Gamma again, as Gb + Gs: Gb the prefix sums of the gates' multiples
+        // of kGateStep (exact), Gs those of the remainders (at most
+        // 16 kGateStep in magnitude).  A difference Gamma_t - Gamma_s is then
+        // an exact difference plus a small one, whatever the decays before
+        // s: no cancellation against a large prefix, and no inf - inf.
+        // The per-token gates again, from the raw gate row (same arithmetic,
+        // same values), then two passes through this lane's table rows, four
+        // channels at a time, so few values are live at once.
+        {
+          const int64_t tok = c0 + n < t1 ? c0 + n : t1 - 1;
+          RunN<false, CPL> xr;
+          xr.load(a.raw_gate, (tok * a.HV + hv) * DK + chan0[p]);
+          float xg[CPL], gg[CPL];
+          xr.unpack(xg);
+          log2_decays<CPL>(a.gate_mode, amp2, lb2, live, xg, dtb[p], gg);
+#pragma unroll
+          for (int j = 0; j < CPL; j += 4)
+            *reinterpret_cast<f32x4*>(&sh.pg[w][n][CPL * g + j]) = f32x4{gg[j], gg[j + 1], gg[j + 2], gg[j + 3]};
+        }
+#pragma unroll
+        for (int j = 0; j < CPL; j += 4) {
+          const f32x4 x4 = *reinterpret_cast<const f32x4*>(&sh.pg[w][n][CPL * g + j]);
+          f32x4 b4, r4;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float gj = fmaxf(x4[i], -kGateFloor);
+            const float gb = kGateStep * ceilf(gj * (1.0f / kGateStep));
+            b4[i] = row_scan(gb);
+            r4[i] = row_scan(gj - gb);
+          }
+          *reinterpret_cast<f32x4*>(&sh.pg[w][n][CPL * g + j]) = b4;
+          *reinterpret_cast<f32x4*>(&sh.ps[w][n][CPL * g + j]) = r4;
+        }
+        wave_lds_order();
+#pragma unroll
+        for (int j = 0; j < CPL; j += 4) {
+          const f32x4 b4 = *reinterpret_cast<const f32x4*>(&sh.pg[w][n][CPL * g + j]);
+          const f32x4 r4 = *reinterpret_cast<const f32x4*>(&sh.ps[w][n][CPL * g + j]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float dlast = (dpp_row<kDppRowBcast15, true>(b4[i]) - b4[i]) +
+                                (dpp_row<kDppRowBcast15, true>(r4[i]) - r4[i]);
+            const float eg = exp2_f(b4[i] + r4[i]);
+            egl[j + i] = dpp_row<kDppRowBcast15, true>(eg);
+            kt[j + i] = k[j + i] * eg;
+            qt[j + i] = q[j + i] * eg;
+            sh.kup.store(chan0[p] + j + i, n, k[j + i] * exp2_f(dlast));
+          }
+        }
       }
       sh.kt.template store<CPL>(n, chan0[p], kt);
       sh.qt.template store<CPL>(n, chan0[p], qt);
@@ -685,7 +806,7 @@ kda_prefill_chunks(DecodeArgs a) {
         for (int j = 0; j < CPL; j += 4)
           *reinterpret_cast<f32x4*>(&sh.egl[chan0[p] + j]) = f32x4{egl[j], egl[j + 1], egl[j + 2], egl[j + 3]};
       }
-      if (!__any(wide_lane)) {
+      if (!wide) {
         // this group's P and R parts as one product each
         float kp[CPL], qp[CPL], ks[CPL];
 #pragma unroll
@@ -706,32 +827,10 @@ kda_prefill_chunks(DecodeArgs a) {
         for (int j = 0; j < CPL; j += 4) {
           *reinterpret_cast<f32x4*>(&sh.pq[w][n][CPL * g + j]) = f32x4{q[j], q[j + 1], q[j + 2], q[j + 3]};
           *reinterpret_cast<f32x4*>(&sh.pk[w][n][CPL * g + j]) = f32x4{k[j], k[j + 1], k[j + 2], k[j + 3]};
-          *reinterpret_cast<f32x4*>(&sh.pg[w][n][CPL * g + j]) = f32x4{G[j], G[j + 1], G[j + 2], G[j + 3]};
         }
         wave_lds_order();
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int pi = lane + 64 * r;
-          const int tt = pi / kChunk, ss = pi % kChunk;
-          if (ss <= tt) {
-            float pv = 0.0f, rv = 0.0f;
-            for (int d = 0; d < CGS; d += 4) {
-              const f32x4 kt4 = *reinterpret_cast<const f32x4*>(&sh.pk[w][tt][d]);
-              const f32x4 qt4 = *reinterpret_cast<const f32x4*>(&sh.pq[w][tt][d]);
-              const f32x4 gt4 = *reinterpret_cast<const f32x4*>(&sh.pg[w][tt][d]);
-              const f32x4 ks4 = *reinterpret_cast<const f32x4*>(&sh.pk[w][ss][d]);
-              const f32x4 gs4 = *reinterpret_cast<const f32x4*>(&sh.pg[w][ss][d]);
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const float e = ks4[j] * exp2_f(fminf(gt4[j] - gs4[j], 0.0f));
-                pv = fmaf(kt4[j], e, pv);
-                rv = fmaf(qt4[j], e, rv);
-              }
-            }
-            pw[r] += pv;
-            rw[r] += rv;
-          }
-        }
+        if (exact) pair_sums<true>(sh, w, lane, pw, rw);
+        else pair_sums<false>(sh, w, lane, pw, rw);
         wave_lds_order();
         any_wide = true;
       }

@@ -1,0 +1,98 @@
+"""GPU parity on the degenerate inputs of the recurrence, against the fp64
+oracle: a zero query (the read returns exactly zero), a zero key (L2 norm of
+a zero vector: nothing is written), gates that decay the state to exactly
+zero (softplus of +inf, and of a large finite value whose exponential
+underflows), gates with no decay (softplus of -inf), and saturated write
+strengths (beta logits of +-inf and of +-1e4).
+
+Each request of the batch walks through the same sequence of planted
+tokens; every other value is the usual seeded draw.
+"""
+import numpy as np
+import pytest
+
+from gated_delta_rule_82_amd import workloads as wl
+from tests import kda_harness as H
+
+pytestmark = pytest.mark.gpu
+
+INF = np.float32(np.inf)
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from gated_delta_rule_82_amd import kda
+    kda.library()
+    return torch
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def plant(inp, infinite_gates=True):
+    """Overwrite tokens 0..8 of every request with the degenerate cases."""
+    cfg = inp.cfg
+    big = INF if infinite_gates else np.float32(1e4)
+    for b in range(cfg.B):
+        t0 = int(inp.cu_seqlens[b])
+        n = int(inp.cu_seqlens[b + 1]) - t0
+        assert n >= 9
+        inp.q[0, t0 + 0] = 0.0                        # zero query: o = 0
+        inp.k[0, t0 + 1] = 0.0                        # zero key: no write
+        inp.raw_gate[0, t0 + 2, :, ::2] = big         # decay to zero (half the rows)
+        inp.raw_gate[0, t0 + 3, :, 1::2] = 1e4        # finite gate, exp underflows
+        inp.raw_gate[0, t0 + 4] = -big                # no decay (softplus gate)
+        inp.beta_logits[0, t0 + 5] = big              # beta = 1
+        inp.beta_logits[0, t0 + 6] = -big             # beta = 0
+        inp.raw_gate[0, t0 + 7] = -1e4
+        inp.beta_logits[0, t0 + 7] = 1e4
+    if cfg.qkv_dtype == "bf16":
+        for name in ("q", "k"):
+            inp.bits[name] = wl.f32_to_bf16_bits(getattr(inp, name))
+    return inp
+
+
+def work(gate, qkv, layout, sdt, DK=32, DV=32, seed=11):
+    return wl.Workload(name="degenerate", B=4, H=2, HV=4, DK=DK, DV=DV, n_slots=7,
+                       cu_seqlens=(0, 9, 21, 30, 50), qkv_dtype=qkv, gate_mode=gate,
+                       lower_bound=-5.0 if gate == wl.LOWER_BOUND else 0.0, seed=seed,
+                       host_state=True, state_layout=layout, state_dtype=sdt)
+
+
+@pytest.mark.parametrize("gate", [wl.SOFTPLUS, wl.LOWER_BOUND])
+@pytest.mark.parametrize("qkv,layout,sdt,DK,DV", [
+    ("f32", "k_first", "f32", 32, 32),
+    ("bf16", "v_first", "f32", 128, 128),
+    ("bf16", "k_first", "f32", 128, 128),
+    ("bf16", "k_first", "bf16", 64, 32),
+])
+def test_decode_degenerate_inputs(torch_cuda, gate, qkv, layout, sdt, DK, DV):
+    cfg = work(gate, qkv, layout, sdt, DK, DV)
+    _say("decode degenerate", gate, qkv, layout, sdt, DK, DV)
+    inp = plant(wl.draw(cfg))
+    stats, _, _ = H.parity_case(inp)
+    print(stats, flush=True)
+
+
+@pytest.mark.parametrize("matmul", ["split_bf16", "f32"])
+@pytest.mark.parametrize("gate", [wl.SOFTPLUS, wl.LOWER_BOUND])
+@pytest.mark.parametrize("layout", ["v_first", "k_first"])
+def test_prefill_degenerate_inputs(torch_cuda, matmul, gate, layout):
+    cfg = work(gate, "bf16", layout, "f32", 128, 128)
+    _say("prefill degenerate", matmul, gate, layout)
+    inp = plant(wl.draw(cfg))
+    stats, _, _ = H.parity_case(inp, entry="prefill", matmul=matmul)
+    print(stats, flush=True)
+
+
+@pytest.mark.parametrize("matmul", ["split_bf16", "f32"])
+def test_prefill_degenerate_finite_gates(torch_cuda, matmul):
+    cfg = work(wl.SOFTPLUS, "bf16", "v_first", "f32", 128, 128)
+    _say("prefill degenerate finite", matmul)
+    inp = plant(wl.draw(cfg), infinite_gates=False)
+    stats, _, _ = H.parity_case(inp, entry="prefill", matmul=matmul)
+    print(stats, flush=True)
