@@ -391,6 +391,53 @@ __device__ __forceinline__ float load_elem(const void* base, int64_t off) {
   else return static_cast<const float*>(base)[off];
 }
 
+// The state slab moves through a raw buffer resource spanning exactly the
+// (slot, head) tile: a lane keeps one 32-bit byte offset and every access
+// adds a constant, instead of a 64-bit address per element.
+constexpr int kRawBufferWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_resource(void* tile, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(tile, static_cast<short>(0), bytes, kRawBufferWord3);
+}
+
+// N (1 or 4) consecutive state elements at byte offset voff + soff.
+template <bool BF16, int N>
+__device__ __forceinline__ void load_state(__amdgpu_buffer_rsrc_t r, int voff, int soff, float* x) {
+  if constexpr (BF16 && N == 4) {
+    const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+    x[0] = bf16_to_f32(w.x & 0xffffu);
+    x[1] = __uint_as_float(w.x & 0xffff0000u);
+    x[2] = bf16_to_f32(w.y & 0xffffu);
+    x[3] = __uint_as_float(w.y & 0xffff0000u);
+  } else if constexpr (BF16) {
+    x[0] = bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0));
+  } else if constexpr (N == 4) {
+    const f32x4 w = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+    x[0] = w.x;
+    x[1] = w.y;
+    x[2] = w.z;
+    x[3] = w.w;
+  } else {
+    x[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));   // bits, not a conversion
+  }
+}
+
+template <bool BF16, int N>
+__device__ __forceinline__ void store_state(__amdgpu_buffer_rsrc_t r, int voff, int soff, const float* x) {
+  if constexpr (BF16 && N == 4) {
+    const u32x2 w = {f32_to_bf16_rne(x[0]) | (f32_to_bf16_rne(x[1]) << 16),
+                     f32_to_bf16_rne(x[2]) | (f32_to_bf16_rne(x[3]) << 16)};
+    __builtin_amdgcn_raw_buffer_store_b64(w, r, voff, soff, 0);
+  } else if constexpr (BF16) {
+    __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(f32_to_bf16_rne(x[0])), r, voff, soff, 0);
+  } else if constexpr (N == 4) {
+    const f32x4 w = {x[0], x[1], x[2], x[3]};
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, w), r, voff, soff, 0);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x[0]), r, voff, soff, 0);
+  }
+}
+
 template <bool BF16>
 __device__ __forceinline__ void store_elem(void* base, int64_t off, float x) {
   if constexpr (BF16) static_cast<uint16_t*>(base)[off] = static_cast<uint16_t>(f32_to_bf16_rne(x));
@@ -624,17 +671,32 @@ kda_prefill_chunks(DecodeArgs a) {
   // ---- the state slab into the accumulators: S[mt][nt][i] is
   // S[16 mt + 4g + i][vcol0 + 16 nt + n]
   f32x4 S[MT][NTV];
-  const int64_t tile = (static_cast<int64_t>(slot) * a.HV + hv) * DK * DV;
+  // Element (d, v) of the tile sits at v * DK + d (value-first) or d * DV + v
+  // (key-first); with d = 16 mt + 4 g + i and v = vcol0 + 16 nt + n the
+  // lane's part is lane_off, the rest a constant per (mt, nt, i).
+  constexpr int kElem = SBF16 ? 2 : 4;
+  char* const tile = static_cast<char*>(a.state_pool) +
+                     (static_cast<int64_t>(slot) * a.HV + hv) * (DK * DV * kElem);
+  const __amdgpu_buffer_rsrc_t st_res = tile_resource(tile, DK * DV * kElem);
+  const int lane_off = (VFIRST ? (vcol0 + n) * DK + 4 * g : 4 * g * DV + vcol0 + n) * kElem;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < NTV; ++nt)
+    for (int nt = 0; nt < NTV; ++nt) {
+      if constexpr (VFIRST) {   // four consecutive keys: one access
+        float x[4];
+        load_state<SBF16, 4>(st_res, lane_off, (16 * nt * DK + 16 * mt) * kElem, x);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int d = 16 * mt + 4 * g + i, v = vcol0 + 16 * nt + n;
-        const int64_t off = VFIRST ? static_cast<int64_t>(v) * DK + d : static_cast<int64_t>(d) * DV + v;
-        S[mt][nt][i] = load_elem<SBF16>(a.state_pool, tile + off);
+        for (int i = 0; i < 4; ++i) S[mt][nt][i] = x[i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float x;
+          load_state<SBF16, 1>(st_res, lane_off, ((16 * mt + i) * DV + 16 * nt) * kElem, &x);
+          S[mt][nt][i] = x;
+        }
       }
+    }
 
   // channel groups of this wave: group w + NW p covers channels
   // [CGS (w + NW p), +CGS); this lane's CPL start at chan0[p]
@@ -997,13 +1059,18 @@ kda_prefill_chunks(DecodeArgs a) {
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < NTV; ++nt)
+    for (int nt = 0; nt < NTV; ++nt) {
+      if constexpr (VFIRST) {
+        const float x[4] = {S[mt][nt][0], S[mt][nt][1], S[mt][nt][2], S[mt][nt][3]};
+        store_state<SBF16, 4>(st_res, lane_off, (16 * nt * DK + 16 * mt) * kElem, x);
+      } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int d = 16 * mt + 4 * g + i, v = vcol0 + 16 * nt + n;
-        const int64_t off = VFIRST ? static_cast<int64_t>(v) * DK + d : static_cast<int64_t>(d) * DV + v;
-        store_elem<SBF16>(a.state_pool, tile + off, S[mt][nt][i]);
+        for (int i = 0; i < 4; ++i) {
+          const float x = S[mt][nt][i];
+          store_state<SBF16, 1>(st_res, lane_off, ((16 * mt + i) * DV + 16 * nt) * kElem, &x);
+        }
       }
+    }
 }
 
 // ---------------------------------------------------------------------------
