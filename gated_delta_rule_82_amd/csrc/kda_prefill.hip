@@ -99,12 +99,13 @@ constexpr float kSafeSpan = 80.0f;  // largest decay span of the one-product P, 
 // in fp32 they carry an error near ulp(|Gamma|), harmless while a chunk's
 // decay span stays within kExactSpan (in log2 units; ulp(512) = 2^-14 gives
 // factor errors of order 1e-5).  A wider span, or a non-finite one, splits
-// each token's log2-decay g into a multiple of kGateStep, whose prefix sums
-// are exact in fp32, and a remainder in (-kGateStep, 0]; g is first raised
-// to -kGateFloor (exp2 of it is already 0 in fp32), which keeps an infinite
-// decay finite: prefix sums stay below 2^24 in magnitude.
+// each token's log2-decay g into an integer, whose prefix sums are exact in
+// fp32, and a remainder in (-1, 0], whose prefix sums stay within 16
+// (ulp 2^-20); g is first raised to -kGateFloor (exp2 of it is already 0 in
+// fp32), which keeps an infinite decay finite and the integer sums below
+// 2^24.
 constexpr float kExactSpan = 512.0f;
-constexpr float kGateStep = 8.0f;
+constexpr float kGateStep = 1.0f;
 constexpr float kGateFloor = 1048576.0f;   // 2^20
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr int kPT = kChunk + 4;     // pitch of the 16-column LDS tables
@@ -591,8 +592,8 @@ __device__ __forceinline__ void log2_decays(int gate_mode, float amp2, float lb2
 
 // The pair-by-pair parts of P_raw and R_raw^T over one wave's channel
 // group: lane pairs (t, s), s <= t, four per lane.  The table rows hold raw
-// q and k and Gamma, the latter as one prefix sum or (EXACT) as its exact
-// multiples of kGateStep in pg and the remainders in ps.
+// q and k and Gamma, the latter as one prefix sum or (EXACT) as the exact
+// sums of integer parts in pg and of the remainders in ps.
 template <bool EXACT, class Shared>
 __device__ __forceinline__ void pair_sums(const Shared& sh, int w, int lane, float (&pw)[4], float (&rw)[4]) {
 #pragma unroll
@@ -811,9 +812,9 @@ kda_prefill_chunks(DecodeArgs a) {
             *reinterpret_cast<f32x4*>(&sh.pg[w][n][CPL * g + j]) = f32x4{G[j], G[j + 1], G[j + 2], G[j + 3]};
         }
       } else {
-        // Gamma again, as Gb + Gs: Gb the prefix sums of the gates' multiples
-        // of kGateStep (exact), Gs those of the remainders (at most
-        // 16 kGateStep in magnitude).  A difference Gamma_t - Gamma_s is then
+        // Gamma again, as Gb + Gs: Gb the prefix sums of the gates' integer
+        // parts (exact), Gs those of the remainders (at most 16 in
+        // magnitude).  A difference Gamma_t - Gamma_s is then
         // an exact difference plus a small one, whatever the decays before
         // s: no cancellation against a large prefix, and no inf - inf.
         // The per-token gates again, from the raw gate row (same arithmetic,
