@@ -789,6 +789,12 @@ kda_prefill_chunks(DecodeArgs a) {
         wide_lane |= !(-GL[j] <= kSafeSpan * kLog2e);
       }
       float kt[CPL], qt[CPL], egl[CPL];
+      // Kup's factor exp(Gamma_last - Gamma_s) is exactly 1 for the last
+      // real token.  In a ragged chunk Gamma_last is read from lane 15,
+      // whose prefix sum holds the same terms as lane m - 1's (the padding
+      // adds zeros) added in another order, so the difference would be an
+      // ulp of |Gamma| instead of 0.
+      const bool last_real = n == m - 1;
       const bool wide = __any(wide_lane);
       bool exact = false;
       if (wide) {
@@ -804,7 +810,7 @@ kda_prefill_chunks(DecodeArgs a) {
           egl[j] = dpp_row<kDppRowBcast15, true>(eg);   // exp(Gamma_last), from token 15
           kt[j] = k[j] * eg;
           qt[j] = q[j] * eg;
-          sh.kup.store(chan0[p] + j, n, k[j] * exp2_f(GL[j] - G[j]));
+          sh.kup.store(chan0[p] + j, n, last_real ? k[j] : k[j] * exp2_f(GL[j] - G[j]));
         }
         if (wide) {
 #pragma unroll
@@ -858,7 +864,7 @@ kda_prefill_chunks(DecodeArgs a) {
             egl[j + i] = dpp_row<kDppRowBcast15, true>(eg);
             kt[j + i] = k[j + i] * eg;
             qt[j + i] = q[j + i] * eg;
-            sh.kup.store(chan0[p] + j + i, n, k[j + i] * exp2_f(dlast));
+            sh.kup.store(chan0[p] + j + i, n, last_real ? k[j + i] : k[j + i] * exp2_f(dlast));
           }
         }
       }
