@@ -542,8 +542,11 @@ __global__ __launch_bounds__(kWave) void kda_decode_vfirst(const DecodeArgs a) {
   // 512 / dk rows one load instruction then covers, else 4.  The 8 keys are
   // two groups of 4: adjacent (one 16-byte access of 8 bf16) for a bf16 pool,
   // dk/2 apart (two 16-byte fp32 accesses, each instruction reading half
-  // rows) for an fp32 pool.
-  constexpr int EPL = (kWave * 8 / DK <= CW) ? 8 : 4;
+  // rows) for an fp32 pool -- which only keeps whole cache lines while a
+  // half row is at least 128 bytes, dk >= 64; smaller fp32 rows take 4 keys
+  // per lane and each instruction reads whole rows (d = 32 value-first:
+  // 724 -> 568 us at the same bytes).
+  constexpr int EPL = (kWave * 8 / DK <= CW && (SBF16 || DK >= 64)) ? 8 : 4;
   constexpr int Q = EPL / 4;              // 4-key groups per lane
   constexpr bool ONE_ACCESS = SBF16 && EPL == 8;
   constexpr int KSTEP = ONE_ACCESS ? 8 : 4;       // keys between neighbouring lanes
@@ -700,14 +703,22 @@ __global__ __launch_bounds__(kWave) void kda_decode_vfirst(const DecodeArgs a) {
 // per request a wave is almost all state traffic, and at dk = dv = 128 two
 // waves per SIMD stream an fp32 pool faster than four (measured on the
 // 96-head batch: key-first 545 -> 536 us, value-first 570 -> 549 us; the
-// 32-head batch key-first 55.7 -> 52.6 us).  Multi-token batches and bf16
-// pools lose with the cap, and so does a value-first batch of fewer than
-// kCapMinWaves waves (the 32-head batch, 52.1 -> 54.5 us): those keep the
-// full occupancy.  The cap is taken through dynamic LDS that the kernel
-// never touches: at kCappedLds bytes per one-wave workgroup, eight
-// workgroups fill a CU's 160 KiB, two waves per SIMD.
-constexpr size_t kCappedLds = 18560;
+// 32-head batch key-first 55.7 -> 52.6 us).  That is about 128 KiB of state
+// in flight per CU; at dk = dv = 64 (half the bytes per wave) the same
+// amount is four waves per SIMD instead of six (1024 requests x 96 heads:
+// key-first 579 -> 566 us, value-first 579 -> 562 us).  Multi-token batches and
+// bf16 pools lose with the cap, and so does a value-first batch of fewer
+// than kCapMinWaves waves (the 32-head batch, 52.1 -> 54.5 us): those keep
+// the full occupancy.  The cap is taken through dynamic LDS that the
+// kernel never touches: capped_lds(N) bytes per one-wave workgroup let N
+// workgroups fill a CU's 160 KiB.
 constexpr int64_t kCapMinWaves = 16384;   // four rounds at four waves per SIMD
+constexpr size_t kCuLds = 163840;
+
+constexpr size_t capped_lds(int workgroups_per_cu) {   // a little over 160 KiB / (N + 1)
+  return kCuLds * 10 / (10 * workgroups_per_cu + 8) / 64 * 64;
+}
+static_assert(capped_lds(8) == 18560, "two waves per SIMD");
 
 template <int DK, int DV>
 constexpr size_t static_lds() {   // the kernels' tables: red_tab, upd_tab, u_tab
@@ -722,10 +733,12 @@ hipError_t launch_one(const DecodeArgs& args, hipStream_t stream) {
   const void* fn = LAYOUT == KDA_STATE_K_FIRST
                        ? reinterpret_cast<const void*>(&kda_decode_kfirst<DK, DV, QBF16, SBF16, CONVV>)
                        : reinterpret_cast<const void*>(&kda_decode_vfirst<DK, DV, QBF16, SBF16, CONVV>);
-  static_assert(static_lds<DK, DV>() < kCappedLds, "cap above the tables");
-  const bool cap = DK == 128 && DV == 128 && !SBF16 && args.T <= args.B &&
+  // workgroups per CU that hold about 128 KiB of state: 8 at d = 128, 16 at 64
+  constexpr int kCapWgs = 32768 / (DK * CW);
+  static_assert(static_lds<DK, DV>() < capped_lds(kCapWgs), "cap above the tables");
+  const bool cap = DK >= 64 && DV >= 64 && !SBF16 && args.T <= args.B &&
                    (LAYOUT == KDA_STATE_K_FIRST || nwg >= kCapMinWaves);
-  const size_t dyn_lds = cap ? kCappedLds - static_lds<DK, DV>() : 0;
+  const size_t dyn_lds = cap ? capped_lds(kCapWgs) - static_lds<DK, DV>() : 0;
   return hipLaunchKernel(fn, dim3(static_cast<uint32_t>(nwg)), dim3(kWave), kargs, dyn_lds, stream);
 }
 
