@@ -105,11 +105,10 @@ struct StateIO {
     if constexpr (SBF16 && N == 8) {
       u32x4 w;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = f32_to_bf16_rne(x[2 * e]) | (f32_to_bf16_rne(x[2 * e + 1]) << 16);
+      for (int e = 0; e < 4; ++e) w[e] = f32x2_to_bf16x2_rne(x[2 * e], x[2 * e + 1]);
       __builtin_amdgcn_raw_buffer_store_b128(w, r, voff, soff, POLICY);
     } else if constexpr (SBF16) {
-      const u32x2 w = {f32_to_bf16_rne(x[0]) | (f32_to_bf16_rne(x[1]) << 16),
-                       f32_to_bf16_rne(x[2]) | (f32_to_bf16_rne(x[3]) << 16)};
+      const u32x2 w = {f32x2_to_bf16x2_rne(x[0], x[1]), f32x2_to_bf16x2_rne(x[2], x[3])};
       __builtin_amdgcn_raw_buffer_store_b64(w, r, voff, soff, POLICY);
     } else {
       const f32x4 w = {x[0], x[1], x[2], x[3]};

@@ -24,14 +24,21 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
 }
 
 // fp32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN.
-// Both candidates are computed and one is selected: written as a branch,
-// the NaN test became divergent control flow around each conversion, and
-// ahead of a packed multi-value store that code produced wrong words.
+// The gfx950 conversion instruction (v_cvt_pk_bf16_f32) does it for two
+// values at once; on the GPU it matched the bit formula
+// (u + 0x7fff + ((u >> 16) & 1)) >> 16, NaN quieted, on every one of 16.7 M
+// inputs (ties at every exponent, denormals, infinities, NaN payloads).
+// The formula costs about five instructions per value, which is what a
+// multi-token decode on a bf16 pool is short of.
+typedef __bf16 kda_bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2_rne(float lo, float hi) {
+  const kda_bf16x2 h = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, h);   // lo in bits 0..15
+}
+
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
-  const uint32_t u = __float_as_uint(x);
-  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-  const uint32_t quiet_nan = (u >> 16) | 0x40u;
-  return (u & 0x7fffffffu) > 0x7f800000u ? quiet_nan : rounded;
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
 
 // Transcendentals use the hardware exp2 / log2 / rcp / rsqrt instructions

@@ -426,8 +426,7 @@ __device__ __forceinline__ void load_state(__amdgpu_buffer_rsrc_t r, int voff, i
 template <bool BF16, int N>
 __device__ __forceinline__ void store_state(__amdgpu_buffer_rsrc_t r, int voff, int soff, const float* x) {
   if constexpr (BF16 && N == 4) {
-    const u32x2 w = {f32_to_bf16_rne(x[0]) | (f32_to_bf16_rne(x[1]) << 16),
-                     f32_to_bf16_rne(x[2]) | (f32_to_bf16_rne(x[3]) << 16)};
+    const u32x2 w = {f32x2_to_bf16x2_rne(x[0], x[1]), f32x2_to_bf16x2_rne(x[2], x[3])};
     __builtin_amdgcn_raw_buffer_store_b64(w, r, voff, soff, 0);
   } else if constexpr (BF16) {
     __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(f32_to_bf16_rne(x[0])), r, voff, soff, 0);
