@@ -1,0 +1,69 @@
+"""GPU parity on every tile of the full-size decode batches, in the launch
+configuration bench.py times (one kda_decode call over the whole batch).
+
+The other full-size cases check sampled tiles; the oracle is fast enough to
+take every (request, head) tile of these batches, in chunks so that the
+host holds a bounded number of fp64 tiles at a time.  Bounds are those of
+tests/kda_harness.py (required and tight), and every slot outside
+state_indices must be bit-identical after the call.
+"""
+import numpy as np
+import pytest
+
+from gated_delta_rule_82_amd import workloads as wl
+from tests import kda_harness as H
+
+pytestmark = pytest.mark.gpu
+
+CHUNK = 4096   # tiles per oracle pass
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from gated_delta_rule_82_amd import kda
+    kda.library()
+    return torch
+
+
+@pytest.mark.parametrize("name,layout,sdt", [
+    ("wide_b256_h96", "k_first", "f32"),      # the bench workload
+    ("wide_b256_h96", "v_first", "f32"),
+    ("wide_b256_h96", "k_first", "bf16"),
+    ("stress_b1024_n4", "k_first", "f32"),
+])
+def test_every_tile(torch_cuda, name, layout, sdt):
+    torch = torch_cuda
+    cfg = wl.preset(name, state_layout=layout, state_dtype=sdt)
+    print("[case] every tile", name, layout, sdt, cfg.B * cfg.HV, "tiles", flush=True)
+    inp = wl.draw(cfg)
+    dev = wl.to_device(inp)
+    pool = wl.device_pool(inp)
+    tiles = [(b, hv) for b in range(cfg.B) for hv in range(cfg.HV)]
+    slots = [int(inp.state_indices[b]) for b, _ in tiles]
+    hvs = [hv for _, hv in tiles]
+    init = H.gather_tiles(pool, slots, hvs)
+    untouched = np.setdiff1d(np.arange(cfg.n_slots), inp.state_indices)
+    idx = torch.as_tensor(untouched, device=pool.device)
+    before = pool[idx].clone()
+    out = wl.empty_out(inp)
+    out.fill_(float("nan"))
+    H.run_gpu(inp, dev, pool, out)
+    torch.cuda.synchronize()
+    assert torch.equal(pool[idx], before), "a slot outside state_indices changed"
+    del before
+    after = H.gather_tiles(pool, slots, hvs)
+    og = H.out_to_f64(out)
+    worst = {}
+    for i0 in range(0, len(tiles), CHUNK):
+        tl = tiles[i0:i0 + CHUNK]
+        oref, pref = H.oracle_tiles(inp, tl, list(init[i0:i0 + CHUNK]))
+        st = H.compare_outputs(inp, tl, og, oref)
+        st.update(H.compare_states(list(after[i0:i0 + CHUNK]),
+                                   [pref[(slots[i0 + k], hv)] for k, (_, hv) in enumerate(tl)],
+                                   cfg.state_dtype))
+        for k, v in st.items():
+            worst[k] = max(worst.get(k, 0.0), v)
+    print(worst, flush=True)
