@@ -8,24 +8,34 @@ A step is one kda_decode call over one batch of the workload (default: the
 state pool of 512 slots).  All inputs are resident in HBM before timing.
 Prints one JSON line on stdout; progress goes to stderr.
 
+Decode steps rotate state_indices over disjoint slot sets (as many as the
+pool holds, --no-rotate keeps one), so that consecutive steps touch
+different state tiles and the 256 MB Infinity Cache cannot serve a batch
+whose touched state would fit in it.
+
 --prefill times kda_prefill instead (the chunked whole-sequence form on the
 matrix cores; default workload B=8 x 2048 tokens, 96 heads, value-first
-fp32 state): value is tokens x heads per second, and the roofline is the
-matrix one -- algorithmic flops of the chunk form (X, Y, the state update,
-U, O and the P, R products; 16-token chunks, a ragged chunk counted whole)
-over the mean kernel time, against the dense bf16 peak (split-bf16
-products) or the fp32 matrix peak.
+fp32 state): value is tokens x heads per second.  Its roofline is the
+binding one of two floors: HBM (algorithmic bytes / 8 TB/s) and the matrix
+unit (algorithmic flops of the chunk form -- X, Y, the state update, U, O
+and the P, R products; 16-token chunks, a ragged chunk counted whole --
+times three for split-bf16, whose fp32 product is three bf16 products, over
+the dense bf16 peak; or once over the fp32 matrix peak).
 
 Fields beyond the common ones:
-  roofline      HBM roofline of the decode kernel: achieved = algorithmic
+  roofline      roofline of the dominant kernel: achieved = algorithmic
                 bytes per launch (state read + write of every active tile,
                 plus every token tensor once) / mean kernel time measured
                 with HIP events on the launch stream; peak 8000 GB/s;
                 traffic = HBM bytes per launch from the committed rocprofv3
                 FETCH_SIZE / WRITE_SIZE summary (null when the kernel source
                 changed since the counters were taken).
-  cpu_baseline  the fp64 oracle timed on host cores on a bounded sample of
-                the same workload (one BLAS thread).
+  copy_ceiling  the fastest of the hand-written streaming copies of
+                libkda_bench.so (and torch's copies) over the same byte
+                count: the practical HBM ceiling on this machine.
+  cpu_baseline  the fp64 oracle timed on every host core (one worker
+                process per core, started before any GPU call, one BLAS
+                thread each) on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -87,87 +97,192 @@ def committed_traffic(workload: str, op: str = "kda_decode"):
     return float(m_bytes.group(1)), path
 
 
-def cpu_baseline(inp, pool_t, budget_s: float, heads_per_step=None):
-    """Time the fp64 oracle on the workload's (request, head) tiles in order
-    (wrapping around to further passes), one BLAS thread, until about
-    ``budget_s`` seconds of work are done.  A step is up to 8 requests with
-    all their heads, or ``heads_per_step`` heads of one request."""
+# State a forked oracle worker inherits from the parent (copy-on-write): the
+# drawn workload, set before the pool is created.
+_CPU_INPUT = {}
+
+
+def _cpu_worker_init():
     from threadpoolctl import threadpool_limits
-    import torch
+    _CPU_INPUT["limits"] = threadpool_limits(limits=1)
+
+
+def _cpu_steps(cfg, heads_per_step):
+    """The baseline's units of work: (b0, b1, hv0, hv1) request and value-head
+    ranges -- 8 requests with all their heads, or ``heads_per_step`` heads
+    (a multiple of the GQA group) of one request."""
+    if heads_per_step is None:
+        return [(b, min(b + 8, cfg.B), 0, cfg.HV) for b in range(0, cfg.B, 8)]
+    per = max(cfg.G, heads_per_step // cfg.G * cfg.G)
+    return [(b, b + 1, hv, min(hv + per, cfg.HV)) for b in range(cfg.B) for hv in range(0, cfg.HV, per)]
+
+
+def _cpu_worker_run(args):
+    """One worker's share of the oracle baseline: the workload's units of
+    work in order from its own starting point (wrapping around), each given
+    to the oracle as the token rows and heads it covers, with initial states
+    taken from a bank of tiles drawn from N(0, sigma) on the host (the
+    distribution the device pool is filled with), until ``budget_s``
+    seconds of oracle time are done."""
+    import numpy as np
     from oracle import kda_oracle as ko
-
-    def gather_tiles(slots, hvs):
-        s = torch.as_tensor(slots, dtype=torch.int64, device=pool_t.device)
-        h = torch.as_tensor(hvs, dtype=torch.int64, device=pool_t.device)
-        return pool_t[s, h].float().cpu().numpy()
-
+    wid, nworkers, budget_s, heads_per_step = args
+    inp = _CPU_INPUT["inp"]
     cfg = inp.cfg
     lb = cfg.lower_bound if cfg.gate_mode == "lower_bound" else None
-    order = [(bb, hv) for bb in range(cfg.B) for hv in range(cfg.HV)]
-    per = heads_per_step or 8 * cfg.HV
-    done_tiles, done_th, done_state, elapsed = 0, 0, 0, 0.0
-    with threadpool_limits(limits=1):
-        i = 0
-        while elapsed < budget_s:
-            if i >= len(order):     # whole batch done: start another pass
-                i = 0
-            tiles = order[i:i + per]
-            valid = [(bb, hv) for bb, hv in tiles if inp.state_indices[bb] >= 0]
-            init = gather_tiles([int(inp.state_indices[bb]) for bb, _ in valid],
-                                [hv for _, hv in valid])
-            pool = {(int(inp.state_indices[bb]), hv): S for (bb, hv), S in zip(valid, init)}
-            t0 = time.perf_counter()
-            ko.kda_decode(inp.q, inp.k, inp.v, inp.raw_gate, inp.beta_logits, inp.a_log,
-                          inp.dt_bias, inp.cu_seqlens, pool, inp.state_indices, tiles=tiles,
-                          gate_mode=cfg.gate_mode, lower_bound=lb, state_layout=cfg.state_layout,
-                          state_dtype=cfg.state_dtype)
-            elapsed += time.perf_counter() - t0
-            for bb, hv in tiles:
-                n = int(inp.cu_seqlens[bb + 1] - inp.cu_seqlens[bb])
-                done_th += n
-                if n > 0 and inp.state_indices[bb] >= 0:
-                    done_state += 2 * cfg.DK * cfg.DV * cfg.state_elem_bytes
-            done_tiles += len(tiles)
-            i += per
-    total = len(order)
+    steps = _cpu_steps(cfg, heads_per_step)
+    rng = np.random.default_rng(1000 + wid)
+    shape = (cfg.DV, cfg.DK) if cfg.state_layout == "v_first" else (cfg.DK, cfg.DV)
+    bank = (rng.standard_normal((97,) + shape, dtype=np.float32) * np.float32(cfg.state_sigma))
+    cu = np.asarray(inp.cu_seqlens, dtype=np.int64)
+    i = wid * len(steps) // nworkers
+    done_tiles = done_th = done_state = 0
+    elapsed = 0.0
+    while elapsed < budget_s:
+        b0, b1, hv0, hv1 = steps[i % len(steps)]
+        t0, t1 = int(cu[b0]), int(cu[b1])
+        h0, h1 = hv0 // cfg.G, (hv1 - 1) // cfg.G + 1
+        idx = inp.state_indices[b0:b1]
+        tiles = [(bb, hv) for bb in range(b1 - b0) for hv in range(hv1 - hv0)]
+        pool = {(int(idx[bb]), hv): bank[(done_tiles + n) % len(bank)]
+                for n, (bb, hv) in enumerate(tiles) if idx[bb] >= 0}
+        start = time.perf_counter()
+        ko.kda_decode(inp.q[:, t0:t1, h0:h1], inp.k[:, t0:t1, h0:h1], inp.v[:, t0:t1, hv0:hv1],
+                      inp.raw_gate[:, t0:t1, hv0:hv1], inp.beta_logits[:, t0:t1, hv0:hv1],
+                      inp.a_log[hv0:hv1], inp.dt_bias[hv0:hv1], cu[b0:b1 + 1] - t0, pool, idx,
+                      tiles=tiles, gate_mode=cfg.gate_mode, lower_bound=lb,
+                      state_layout=cfg.state_layout, state_dtype=cfg.state_dtype)
+        elapsed += time.perf_counter() - start
+        for bb, hv in tiles:
+            n = int(cu[b0 + bb + 1] - cu[b0 + bb])
+            done_th += n
+            if n > 0 and idx[bb] >= 0:
+                done_state += 2 * cfg.DK * cfg.DV * cfg.state_elem_bytes
+        done_tiles += len(tiles)
+        i += 1
+    return done_tiles, done_th, done_state, elapsed
+
+
+def start_cpu_pool(inp):
+    """Fork one oracle worker per host core.  Called before anything touches
+    the GPU, so the children start from a process with no HIP state."""
+    import multiprocessing
+    _CPU_INPUT["inp"] = inp
+    n = len(os.sched_getaffinity(0))
+    pool = multiprocessing.get_context("fork").Pool(n, initializer=_cpu_worker_init)
+    return pool, n
+
+
+def cpu_baseline(cpu_pool, inp, budget_s: float, heads_per_step=None):
+    """Time the fp64 oracle on every worker of ``cpu_pool`` at once: each
+    takes the workload's (request, head) tiles in order from its own offset
+    (wrapping around), a unit of work being up to 8 requests with all their
+    heads or ``heads_per_step`` heads of one request, until ``budget_s``
+    seconds of oracle time.  The rate is the sum of the workers' rates, each
+    its work over its own oracle time (all workers run at once)."""
+    pool, n = cpu_pool
+    cfg = inp.cfg
+    t0 = time.perf_counter()
+    res = pool.map(_cpu_worker_run, [(w, n, budget_s, heads_per_step) for w in range(n)])
+    wall = time.perf_counter() - t0
+    tiles = sum(r[0] for r in res)
+    th = sum(r[1] for r in res)
+    state_rate = sum(r[2] / r[3] for r in res)
+    th_rate = sum(r[1] / r[3] for r in res)
+    total = cfg.B * cfg.HV
     return {
-        "value": round(done_state / elapsed / 1e9, 6),
+        "value": round(state_rate / 1e9, 6),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": n,
         "kind": "oracle",
-        "sample": f"{done_tiles} (request, head) tiles ({done_tiles / total:.3f} passes over the "
-                  f"batch's {total}), all their tokens: {done_th} token-heads in "
-                  f"{elapsed:.1f} s, fp64 numpy, 1 BLAS thread",
-        "tokens_heads_per_s": round(done_th / elapsed, 3),
+        "sample": f"{tiles} (request, head) tiles ({tiles / total:.3f} passes over the batch's "
+                  f"{total}), all their tokens: {th} token-heads, {n} worker processes at once "
+                  f"(one BLAS thread each) for {budget_s:.0f} s of oracle time each "
+                  f"({wall:.1f} s wall), fp64 numpy; initial states from the pool's "
+                  f"N(0, {cfg.state_sigma}) distribution, drawn on the host",
+        "tokens_heads_per_s": round(th_rate, 3),
         "host_cores_available": len(os.sched_getaffinity(0)),
     }
 
 
+COPY_VARIANTS = {"nt_stream": 0, "nt_wave": 1, "wave": 2, "nt_kfirst_slabs": 3}
+
+
+def bench_library():
+    """libkda_bench.so: the hand-written streaming copies (built with the
+    library by gated_delta_rule_82_amd.build; only this script loads it)."""
+    import ctypes
+    from gated_delta_rule_82_amd.build import BENCH_LIB
+    if not os.path.exists(BENCH_LIB):
+        raise RuntimeError(f"{BENCH_LIB} is not built; run `python -m gated_delta_rule_82_amd.build`")
+    lib = ctypes.CDLL(BENCH_LIB)
+    lib.kda_bench_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                   ctypes.c_void_p]
+    lib.kda_bench_copy.restype = ctypes.c_int
+    return lib
+
+
 def copy_ceiling(nbytes: int, reps: int = 10):
-    """Plain streaming copies moving ``nbytes`` (half read, half written):
-    torch's device-to-device copy and an elementwise multiply-by-one kernel.
-    Returns {name: GB/s of read + write bytes}; both also serve as the
-    known-size reference kernels for the HBM byte counters."""
+    """Streaming copies moving ``nbytes`` (half read, half written), each
+    buffer pair rotated over enough copies that the 256 MB cache cannot
+    serve them: the hand-written copies of libkda_bench.so and torch's
+    device-to-device and elementwise copies.  Returns {name: GB/s of read +
+    write bytes} (mean over ``reps`` launches, HIP events on the stream)."""
     import torch
-    n = nbytes // 2 // 4
-    src = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
-    dst = torch.empty_like(src)
-    variants = {"d2d_copy": lambda: dst.copy_(src),
-                "elementwise_copy": lambda: torch.mul(src, 1.0, out=dst)}
+    half = nbytes // 2 // 65536 * 65536
+    sets = max(1, -(-(1 << 29) // half))      # >= 512 MB per rotation
+    src = [torch.empty(half // 4, dtype=torch.float32, device="cuda").fill_(1.0) for _ in range(sets)]
+    dst = [torch.empty_like(x) for x in src]
+    stream = torch.cuda.current_stream()
+    lib = bench_library()
+
+    def hand(v):
+        def run(i):
+            rc = lib.kda_bench_copy(dst[i].data_ptr(), src[i].data_ptr(), half, v, stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"kda_bench_copy failed ({rc})")
+        return run
+
+    variants = {name: hand(v) for name, v in COPY_VARIANTS.items()}
+    variants["torch_d2d_copy"] = lambda i: dst[i].copy_(src[i])
+    variants["torch_elementwise_copy"] = lambda i: torch.mul(src[i], 1.0, out=dst[i])
     res = {}
     for name, fn in variants.items():
-        fn()
+        for i in range(sets):
+            fn(i)
         torch.cuda.synchronize()
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s.record()
-        for _ in range(reps):
-            fn()
-        e.record()
+        s.record(stream)
+        for r in range(reps):
+            fn(r % sets)
+        e.record(stream)
         torch.cuda.synchronize()
         ms = s.elapsed_time(e) / reps
-        res[name] = round(2 * n * 4 / (ms * 1e-3) / 1e9, 1)
+        res[name] = round(2 * half / (ms * 1e-3) / 1e9, 1)
     del src, dst
+    torch.cuda.empty_cache()
     return res
+
+
+def rotation_sets(inp, k: int):
+    """``k`` disjoint assignments of the batch's active requests to pool
+    slots: the drawn state_indices first, then further permutations of the
+    slots it leaves unused (negative indices stay negative)."""
+    import numpy as np
+    cfg = inp.cfg
+    idx = np.asarray(inp.state_indices, dtype=np.int32)
+    active = idx >= 0
+    free = np.setdiff1d(np.arange(cfg.n_slots, dtype=np.int32), idx[active])
+    free = np.random.default_rng(cfg.seed + 7).permutation(free)
+    n = int(active.sum())
+    sets = [idx]
+    for j in range(1, k):
+        if free.size < j * n:
+            break
+        nxt = idx.copy()
+        nxt[active] = free[(j - 1) * n:j * n]
+        sets.append(nxt)
+    return sets
 
 
 def main(argv=None) -> int:
@@ -183,10 +298,15 @@ def main(argv=None) -> int:
                     help="time kda_prefill (chunked, matrix cores) on the prefill workload")
     ap.add_argument("--matmul", choices=("split_bf16", "f32"), default="split_bf16",
                     help="matrix precision of --prefill")
+    ap.add_argument("--gate", choices=("softplus", "lower_bound"), default=None,
+                    help="override the workload's gate mode (lower_bound uses -5)")
     ap.add_argument("--conv", action="store_true",
                     help="time kda_decode_conv: the step with the short convolutions in front")
+    ap.add_argument("--no-rotate", action="store_true",
+                    help="reuse the same state slots every step (by default steps rotate over "
+                         "disjoint slot sets so the 256 MB cache cannot hold the touched state)")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
-                    help="seconds of oracle work for cpu_baseline (0 disables)")
+                    help="seconds of oracle work per host core for cpu_baseline (0 disables)")
     ap.add_argument("--no-copy-ceiling", action="store_true")
     args = ap.parse_args(argv)
 
@@ -200,21 +320,29 @@ def main(argv=None) -> int:
         return 2
 
     import numpy as np
+    from gated_delta_rule_82_amd import workloads as wl
+
+    name = args.workload or (wl.PREFILL_HEADLINE if args.prefill else wl.HEADLINE)
+    over = {k: v for k, v in (("state_layout", args.state_layout), ("state_dtype", args.state_dtype))
+            if v is not None}
+    if args.gate is not None:
+        over["gate_mode"] = args.gate
+        over["lower_bound"] = -5.0 if args.gate == "lower_bound" else 0.0
+    cfg = wl.preset(name, **over)
+    log(f"[bench] workload {name}: {cfg.description}" + (f" (overrides {over})" if over else ""))
+    inp = wl.draw(cfg)
+    # the oracle workers fork here, before anything touches the GPU (the
+    # conv step has no oracle baseline of its own here)
+    cpu_pool = start_cpu_pool(inp) if args.cpu_budget > 0 and not args.conv else None
+
     import torch
     from gated_delta_rule_82_amd import kda
-    from gated_delta_rule_82_amd import workloads as wl
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
     kda.library()     # fail loudly if the HIP library is not built
 
-    name = args.workload or (wl.PREFILL_HEADLINE if args.prefill else wl.HEADLINE)
-    over = {k: v for k, v in (("state_layout", args.state_layout), ("state_dtype", args.state_dtype))
-            if v is not None}
-    cfg = wl.preset(name, **over)
-    log(f"[bench] workload {name}: {cfg.description}")
-    inp = wl.draw(cfg)
     dev = wl.to_device(inp)
     pool = wl.device_pool(inp)
     out = wl.empty_out(inp)
@@ -222,6 +350,10 @@ def main(argv=None) -> int:
     token_b = wl.token_bytes(cfg, inp)
     alg_bytes = state_b + token_b
     tok_heads = inp.T * cfg.HV
+    sets = rotation_sets(inp, 1 if args.no_rotate else max(1, cfg.n_slots // max(cfg.B, 1)))
+    idx_sets = [torch.from_numpy(x.astype(np.int32)).to(pool.device) for x in sets]
+    log(f"[bench] {len(sets)} disjoint slot set(s) of {int((sets[0] >= 0).sum())} requests, "
+        f"{state_b / 2 / 1e6:.0f} MB of state each")
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
@@ -235,24 +367,25 @@ def main(argv=None) -> int:
         alg_bytes += conv_bytes
         torch.cuda.synchronize()
 
-        def step():
+        def step(i):
             kda.decode_conv(out, cd["x_q"], cd["x_k"], cd["x_v"], cd["w_q"], cd["w_k"], cd["w_v"],
                             cd["win_q"], cd["win_k"], cd["win_v"], cd["q_conv"], cd["k_conv"],
                             dev["raw_gate"], dev["beta_logits"], dev["a_log"], dev["dt_bias"],
-                            dev["cu_seqlens"], pool, dev["state_indices"], stream=handle, **mode)
+                            dev["cu_seqlens"], pool, idx_sets[i % len(idx_sets)], stream=handle,
+                            **mode)
     elif args.prefill:
-        def step():
+        def step(i):
             kda.prefill(out, dev["q"], dev["k"], dev["v"], dev["raw_gate"], dev["beta_logits"],
-                        dev["a_log"], dev["dt_bias"], dev["cu_seqlens"], pool, dev["state_indices"],
-                        stream=handle, matmul=args.matmul, **mode)
+                        dev["a_log"], dev["dt_bias"], dev["cu_seqlens"], pool,
+                        idx_sets[i % len(idx_sets)], stream=handle, matmul=args.matmul, **mode)
     else:
-        def step():
+        def step(i):
             kda.decode(out, dev["q"], dev["k"], dev["v"], dev["raw_gate"], dev["beta_logits"],
-                       dev["a_log"], dev["dt_bias"], dev["cu_seqlens"], pool, dev["state_indices"],
-                       stream=handle, **mode)
+                       dev["a_log"], dev["dt_bias"], dev["cu_seqlens"], pool,
+                       idx_sets[i % len(idx_sets)], stream=handle, **mode)
 
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} done; timing {args.steps} steps")
 
@@ -262,7 +395,7 @@ def main(argv=None) -> int:
     t0 = time.perf_counter()
     for i in range(args.steps):
         starts[i].record(stream)
-        step()
+        step(args.warmup + i)
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -271,11 +404,35 @@ def main(argv=None) -> int:
     mean_kernel_ms = float(kernel_ms.mean())
     log(f"[bench] wall {ms_per_step * 1e3:.1f} us/step, kernel mean {mean_kernel_ms * 1e3:.1f} us "
         f"(min {kernel_ms.min() * 1e3:.1f}, max {kernel_ms.max() * 1e3:.1f})")
+    del dev, out
+    torch.cuda.empty_cache()
 
-    if args.prefill:
-        return report_prefill(args, cfg, name, inp, pool, ms_per_step, mean_kernel_ms, alg_bytes,
-                              tok_heads)
+    common = dict(args=args, cfg=cfg, name=name, inp=inp, cpu_pool=cpu_pool,
+                  ms_per_step=ms_per_step, mean_kernel_ms=mean_kernel_ms, alg_bytes=alg_bytes,
+                  tok_heads=tok_heads, rotation=len(sets))
+    try:
+        if args.prefill:
+            del pool
+            torch.cuda.empty_cache()
+            return report_prefill(**common)
+        del pool
+        torch.cuda.empty_cache()
+        return report_decode(state_b=state_b, **common)
+    finally:
+        if cpu_pool is not None:
+            cpu_pool[0].terminate()
 
+
+def measure_copies(nbytes):
+    copies = copy_ceiling(nbytes)
+    best = max(copies, key=copies.get)
+    log(f"[bench] copy ceiling (read+write, {nbytes / 1e9:.2f} GB): {copies}")
+    return copies, best
+
+
+def report_decode(args, cfg, name, inp, cpu_pool, ms_per_step, mean_kernel_ms, alg_bytes,
+                  tok_heads, rotation, state_b):
+    import numpy as np
     value = state_b / (ms_per_step * 1e-3) / 1e9
     achieved = alg_bytes / (mean_kernel_ms * 1e-3) / 1e9
     variant = "" if (cfg.state_layout, cfg.state_dtype) == ("k_first", "f32") else \
@@ -285,16 +442,11 @@ def main(argv=None) -> int:
     traffic, traffic_src = committed_traffic(name + variant)
     log(f"[bench] traffic: {traffic} ({traffic_src})")
 
-    copy_gbps = None
-    if not args.no_copy_ceiling:
-        copies = copy_ceiling(state_b)
-        copy_gbps = max(copies.values())
-        log(f"[bench] copy ceiling (read+write, {state_b / 1e9:.2f} GB): {copies}")
-
+    copies, best = (None, None) if args.no_copy_ceiling else measure_copies(state_b)
     cpu = None
-    if args.cpu_budget > 0:
-        log(f"[bench] cpu_baseline: oracle for ~{args.cpu_budget:.0f} s")
-        cpu = cpu_baseline(inp, pool, args.cpu_budget) if not args.conv else None
+    if cpu_pool is not None:
+        log(f"[bench] cpu_baseline: oracle for ~{args.cpu_budget:.0f} s on {cpu_pool[1]} cores")
+        cpu = cpu_baseline(cpu_pool, inp, args.cpu_budget)
         log(f"[bench] cpu_baseline {cpu['value']} GB/s, {cpu['tokens_heads_per_s']} token-heads/s")
 
     counts = np.diff(inp.cu_seqlens)
@@ -316,16 +468,18 @@ def main(argv=None) -> int:
             "tokens_per_request": cfg.tokens, "total_tokens": inp.T,
             "qkv_dtype": cfg.qkv_dtype, "state_dtype": cfg.state_dtype,
             "state_layout": cfg.state_layout, "gate": cfg.gate_mode,
-            "short_conv": bool(args.conv),
-            "slots": cfg.n_slots, "parallelism": "single GPU",
+            "short_conv": bool(args.conv), "slots": cfg.n_slots,
+            "slot_sets_rotated": rotation, "parallelism": "single GPU",
         },
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
         "tokens_heads_per_s": round(tok_heads / (ms_per_step * 1e-3), 1),
         "state_bytes_per_step": state_b,
         "algorithmic_bytes_per_step": alg_bytes,
         "kernel_us_mean": round(mean_kernel_ms * 1e3, 2),
-        "copy_ceiling_GBps": None if copy_gbps is None else round(copy_gbps, 1),
-        "copy_kernels_GBps": None if copy_gbps is None else copies,
+        "copy_ceiling_GBps": None if copies is None else copies[best],
+        "copy_ceiling_kernel": best,
+        "copy_kernels_GBps": copies,
+        "frac_of_copy_ceiling": None if copies is None else round(achieved / copies[best], 4),
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 3),
@@ -352,26 +506,42 @@ def chunk_flops(dk: int, dv: int) -> int:
     return 2 * (3 * c * dk * dv + 2 * c * c * dv + 2 * c * c * dk)
 
 
-def report_prefill(args, cfg, name, inp, pool, ms_per_step, mean_kernel_ms, alg_bytes, tok_heads):
+# bf16 matrix products per fp32-equivalent product of each precision
+PRODUCTS_PER_FLOP = {"split_bf16": 3, "f32": 1}
+
+
+def report_prefill(args, cfg, name, inp, cpu_pool, ms_per_step, mean_kernel_ms, alg_bytes,
+                   tok_heads, rotation):
     import numpy as np
     counts = np.diff(inp.cu_seqlens)
     active = (counts > 0) & (inp.state_indices >= 0)
     chunks = int((-(-counts[active] // CHUNK)).sum()) * cfg.HV
     flops = chunks * chunk_flops(cfg.DK, cfg.DV)
-    achieved = flops / (mean_kernel_ms * 1e-3) / 1e12
-    peak = MATRIX_PEAK_TFLOPS[args.matmul]
-    hbm = alg_bytes / (mean_kernel_ms * 1e-3) / 1e9
-    variant = f"_{args.matmul}"
+    t_kernel = mean_kernel_ms * 1e-3
+    peak_tf = MATRIX_PEAK_TFLOPS[args.matmul]
+    t_hbm = alg_bytes / (HBM_PEAK_GBPS * 1e9)
+    t_mfma = PRODUCTS_PER_FLOP[args.matmul] * flops / (peak_tf * 1e12)
+    matrix = {"achieved": round(flops / t_kernel / 1e12, 3), "peak": peak_tf, "unit": "TFLOP/s",
+              "products_per_flop": PRODUCTS_PER_FLOP[args.matmul],
+              "floor_us": round(t_mfma * 1e6, 2), "frac": round(t_mfma / t_kernel, 4)}
+    hbm = {"achieved": round(alg_bytes / t_kernel / 1e9, 3), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+           "floor_us": round(t_hbm * 1e6, 2), "frac": round(t_hbm / t_kernel, 4)}
+    variant = f"_{args.matmul}" + ("" if cfg.gate_mode == "lower_bound" else f"_{cfg.gate_mode}")
     traffic, traffic_src = committed_traffic(name + variant, "kda_prefill")
     log(f"[bench] traffic: {traffic} ({traffic_src})")
-    copies = None
-    if not args.no_copy_ceiling:
-        copies = copy_ceiling(alg_bytes)
-        log(f"[bench] copy ceiling (read+write, {alg_bytes / 1e9:.2f} GB): {copies}")
+    if t_hbm >= t_mfma:
+        roof = dict(bound="hbm", **{k: hbm[k] for k in ("achieved", "peak", "unit", "frac")})
+    else:
+        roof = dict(bound="mfma", **{k: matrix[k] for k in ("achieved", "peak", "unit", "frac")})
+    roof["traffic"] = traffic
+    roof["kernel"] = "kda_prefill_chunks<%d,%d,%s q/k/v,%s state,%s,%s>" % (
+        cfg.DK, cfg.DV, cfg.qkv_dtype, cfg.state_dtype, cfg.state_layout.replace("_", ""),
+        args.matmul)
+    copies, best = (None, None) if args.no_copy_ceiling else measure_copies(alg_bytes)
     cpu = None
-    if args.cpu_budget > 0:
-        log(f"[bench] cpu_baseline: oracle for ~{args.cpu_budget:.0f} s")
-        cpu = cpu_baseline(inp, pool, args.cpu_budget, heads_per_step=4)
+    if cpu_pool is not None:
+        log(f"[bench] cpu_baseline: oracle for ~{args.cpu_budget:.0f} s on {cpu_pool[1]} cores")
+        cpu = cpu_baseline(cpu_pool, inp, args.cpu_budget, heads_per_step=4)
         cpu["value"] = cpu["tokens_heads_per_s"]
         cpu["unit"] = "tokens·heads/s"
         log(f"[bench] cpu_baseline {cpu['value']} token-heads/s")
@@ -393,25 +563,19 @@ def report_prefill(args, cfg, name, inp, pool, ms_per_step, mean_kernel_ms, alg_
             "tokens_per_request": cfg.tokens, "total_tokens": inp.T,
             "qkv_dtype": cfg.qkv_dtype, "state_dtype": cfg.state_dtype,
             "state_layout": cfg.state_layout, "gate": cfg.gate_mode, "matmul": args.matmul,
-            "chunk": CHUNK, "slots": cfg.n_slots, "parallelism": "single GPU",
+            "chunk": CHUNK, "slots": cfg.n_slots, "slot_sets_rotated": rotation,
+            "parallelism": "single GPU",
         },
         "kernel_us_mean": round(mean_kernel_ms * 1e3, 2),
         "algorithmic_flops_per_step": flops,
         "algorithmic_bytes_per_step": alg_bytes,
-        "hbm_GBps": round(hbm, 1),
+        "hbm": hbm,
+        "matrix": matrix,
+        "copy_ceiling_GBps": None if copies is None else copies[best],
+        "copy_ceiling_kernel": best,
         "copy_kernels_GBps": copies,
-        "pct_hbm_peak": round(100.0 * hbm / HBM_PEAK_GBPS, 2),
-        "roofline": {
-            "bound": "mfma",
-            "achieved": round(achieved, 3),
-            "peak": peak,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / peak, 4),
-            "traffic": traffic,
-            "kernel": "kda_prefill_chunks<%d,%d,%s q/k/v,%s state,%s,%s>" % (
-                cfg.DK, cfg.DV, cfg.qkv_dtype, cfg.state_dtype, cfg.state_layout.replace("_", ""),
-                args.matmul),
-        },
+        "pct_hbm_peak": round(100.0 * hbm["achieved"] / HBM_PEAK_GBPS, 2),
+        "roofline": roof,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -5,6 +5,8 @@
 The host argument checker is plain C++ (g++); the kernel files (decode and
 chunked prefill) go through hipcc for gfx950 with packed-fp32 instructions
 disabled; hipcc links them into ``gated_delta_rule_82_amd/lib/libkda.so``.
+The benchmark's streaming-copy kernels (its HBM ceiling) build into a
+separate ``lib/libkda_bench.so`` that the library itself never loads.
 """
 from __future__ import annotations
 
@@ -20,6 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libkda.so")
+BENCH_LIB = os.path.join(LIBDIR, "libkda_bench.so")
 ARCH = "gfx950"
 
 HIP_FLAGS = [
@@ -80,7 +83,7 @@ def build(verbose: bool = True) -> str:
     os.makedirs(LIBDIR, exist_ok=True)
     hipcc = _hipcc()
     api_o = os.path.join(BUILD, "kda_api.o")
-    kernels = ("kda_decode", "kda_prefill")
+    kernels = ("kda_decode", "kda_prefill", "bench_copy")
     objs = [os.path.join(BUILD, f"{name}.o") for name in kernels]
     _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", f"-I{INCLUDE}", f"-I{CSRC}",
           "-c", os.path.join(CSRC, "kda_api.cpp"), "-o", api_o], verbose)
@@ -89,10 +92,14 @@ def build(verbose: bool = True) -> str:
              os.path.join(CSRC, f"{name}.hip"), "-o", obj] for name, obj in zip(kernels, objs)]
     _run_all(cmds, verbose)
     tmp = LIB + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", api_o, *objs, "-o", tmp,
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", api_o, *objs[:2], "-o", tmp,
           "-Wl,-z,defs", "-Wl,--no-undefined",
           f"-Wl,--version-script={os.path.join(CSRC, 'libkda.map')}"], verbose)
     os.replace(tmp, LIB)
+    tmp = BENCH_LIB + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", objs[2], "-o", tmp,
+          "-Wl,-z,defs", "-Wl,--no-undefined"], verbose)
+    os.replace(tmp, BENCH_LIB)
     return LIB
 
 

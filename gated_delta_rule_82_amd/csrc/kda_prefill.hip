@@ -551,7 +551,7 @@ struct alignas(16) ChunkShared {
   float pq[NW][kChunk][kGroupChannels + 4];   // raw q, k and Gamma of the wave's
   float pk[NW][kChunk][kGroupChannels + 4];   //   channel group, for the pair-by-
   float pg[NW][kChunk][kGroupChannels + 4];   //   pair P and R (Gamma as its exact
-  float ps[NW][kChunk][kGroupChannels + 4];   //   multiples of 8 and remainders)
+  float ps[NW][kChunk][kGroupChannels + 4];   //   integer parts and remainders)
 };
 
 // Raw inputs of one chunk for one lane: per channel group pass, q, k and

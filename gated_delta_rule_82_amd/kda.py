@@ -236,6 +236,10 @@ def check_host(cu_seqlens, state_indices, T: int, n_slots: int) -> int:
     import numpy as np
     cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
     idx = np.ascontiguousarray(state_indices, dtype=np.int32)
+    if cu.ndim != 1 or idx.ndim != 1 or len(cu) != len(idx) + 1:
+        # kda_check_host reads B + 1 entries of cu_seqlens
+        raise ValueError(f"cu_seqlens needs len(state_indices) + 1 = {len(idx) + 1} entries, "
+                         f"got shape {cu.shape}")
     P = ctypes.POINTER(ctypes.c_int32)
     return library().kda_check_host(cu.ctypes.data_as(P), idx.ctypes.data_as(P),
                                     len(idx), int(T), int(n_slots))

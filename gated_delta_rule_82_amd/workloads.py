@@ -92,6 +92,13 @@ PRESETS = {
         tokens="2048", gate_mode=LOWER_BOUND, lower_bound=-5.0, state_layout="v_first",
         description="prefill: B=8 x 2048 tokens, 96 heads, dk=dv=128, bf16, lower-bound gate, "
                     "value-first fp32 state"),
+    # one long prompt: only 96 (request, head) tiles, fewer than the chip's
+    # 256 compute units
+    "prefill_b1_t16384_h96": Workload(
+        name="prefill_b1_t16384_h96", B=1, H=96, HV=96, DK=128, DV=128, n_slots=2,
+        tokens="16384", gate_mode=LOWER_BOUND, lower_bound=-5.0, state_layout="v_first",
+        description="prefill: B=1 x 16384 tokens, 96 heads, dk=dv=128, bf16, lower-bound gate, "
+                    "value-first fp32 state"),
 }
 
 PREFILL_HEADLINE = "prefill_b8_t2048_h96"

@@ -240,7 +240,11 @@ int kda_prefill(const kda_tensor* out, const kda_tensor* q, const kda_tensor* k,
                 const kda_mode* mode, int32_t matmul, hipStream_t stream);
 
 /*
- * kda_check_host - validate host copies of the decode metadata.
+ * kda_check_host - validate host copies of the decode metadata.  This is a
+ * convention of this library, not an operation of the pages: it checks the
+ * preconditions of the "KdaDecode" tensor contract (cu_seqlens varlen
+ * packing, state_indices into the slotted pool) that kda_decode cannot check
+ * on device-resident data without a device-to-host copy.
  *   cu_seqlens: B + 1 int32 entries; state_indices: B int32 entries.
  * Returns KDA_OK when cu_seqlens[0] == 0, it is non-decreasing and ends at T,
  * and the non-negative indices are distinct and < n_slots; KDA_ERR_NULL for
@@ -250,7 +254,8 @@ int kda_prefill(const kda_tensor* out, const kda_tensor* q, const kda_tensor* k,
 int kda_check_host(const int32_t* cu_seqlens, const int32_t* state_indices,
                    int64_t B, int64_t T, int64_t n_slots);
 
-/* Static description of a status code; never NULL. */
+/* Static description of a status code; never NULL.  A convention of this
+ * library's error reporting (the pages define no error codes). */
 const char* kda_status_string(int status);
 
 /* KDA_ABI_VERSION of the built library. */

@@ -73,6 +73,14 @@ def test_check_host(cu, idx, T, N, expect):
     assert kda.check_host(cu, idx, T, N) == expect
 
 
+def test_check_host_binding_rejects_short_cu_seqlens():
+    # the C function reads B + 1 entries; the binding refuses a shorter array
+    with pytest.raises(ValueError):
+        kda.check_host([0, 3], [2, 0], 5, 4)
+    with pytest.raises(ValueError):
+        kda.check_host([0, 3, 5, 6], [2, 0], 5, 4)
+
+
 def test_check_host_bad_sizes_and_nulls():
     lib = kda.library()
     assert lib.kda_check_host(None, None, 0, 0, 0) == kda.KDA_ERR_NULL

@@ -98,6 +98,33 @@ def test_full_size_other_layouts(torch_cuda, name, sample, layout, sdt):
     torch_cuda.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("layout,sdt", [("k_first", "f32"), ("v_first", "f32"),
+                                        ("k_first", "bf16"), ("v_first", "bf16")])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 32)])
+def test_custom_scale_and_eps(torch_cuda, layout, sdt, dk, dv):
+    """kda_mode.scale and kda_mode.l2_eps replace the defaults dk^-0.5 and
+    1e-6 ("KDA Block TKG" scale parameter and l2_eps default); the oracle
+    runs with the same values.  eps = 16 is large against sum(x^2) ~ dk, so
+    it moves every normalised q and k by several percent."""
+    cfg = small(B=6, H_=2, HV=4, DK=dk, DV=dv, tokens="u:1..6", gate=wl.LOWER_BOUND, lb=-5.0,
+                seed=21 + dk, state_layout=layout, state_dtype=sdt)
+    over = {"scale": 0.3, "l2_eps": 16.0}
+    _say("scale/eps", layout, sdt, dk, dv, over)
+    stats, out_t, _ = H.parity_case(wl.draw(cfg), mode_overrides=over, oracle_mode=over)
+    print("scale/eps", layout, sdt, stats, flush=True)
+    # each override must matter: the oracle with either one left at its
+    # default is far from this output
+    inp = wl.draw(cfg)
+    tiles = [(b, hv) for b in range(cfg.B) for hv in range(cfg.HV)]
+    pool = wl.host_pool(inp)    # in the workload's layout and dtype, as uploaded
+    init = [pool[int(inp.state_indices[b]), hv] for b, hv in tiles if inp.state_indices[b] >= 0]
+    og = H.out_to_f64(out_t)
+    floor = max(stats["out_max_abs"], 1e-6)
+    for partial in ({"scale": 0.3}, {"l2_eps": 16.0}):
+        o_part, _ = H.oracle_tiles(inp, tiles, init, **partial)
+        assert np.max(np.abs(og - o_part)) > 10 * floor, partial
+
+
 def test_ragged_grid_not_multiple_of_8(torch_cuda):
     cfg = small(B=37, H_=5, HV=5, tokens="u:0..3", slots=50, seed=5)
     _say("ragged", cfg)

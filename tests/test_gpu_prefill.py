@@ -73,6 +73,19 @@ def test_prefill_parity(torch_cuda, name, matmul):
 
 
 @pytest.mark.parametrize("matmul", MATMULS)
+@pytest.mark.parametrize("layout,sdt,qkv", [("k_first", "bf16", "bf16"), ("v_first", "f32", "f32")])
+@pytest.mark.parametrize("dk,dv", [(dk, dv) for dk in (32, 64, 128) for dv in (32, 64, 128)])
+def test_prefill_every_specialization(torch_cuda, dk, dv, layout, sdt, qkv, matmul):
+    """Every (dk, dv) pair the prefill dispatches, in both layouts and both
+    matrix precisions; each pair meets a bf16 pool and fp32 q/k/v once."""
+    cfg = work(f"spec_{dk}_{dv}", B=3, H_=2, HV=4, DK=dk, DV=dv, tokens="u:5..45", qkv=qkv,
+               seed=100 + dk + dv, state_layout=layout, state_dtype=sdt)
+    _say("prefill spec", dk, dv, layout, sdt, qkv, matmul)
+    stats, _, _ = H.parity_case(wl.draw(cfg), entry="prefill", matmul=matmul)
+    print("spec", dk, dv, layout, sdt, qkv, matmul, stats, flush=True)
+
+
+@pytest.mark.parametrize("matmul", MATMULS)
 def test_prefill_long_request(torch_cuda, matmul):
     """One 6000-token request (375 chunks): the error must not grow with length."""
     cfg = work("long", B=1, H_=1, HV=2, DK=128, DV=128, tokens="6000", seed=9, state_layout="v_first")
@@ -83,11 +96,23 @@ def test_prefill_long_request(torch_cuda, matmul):
 
 def test_prefill_headline_sampled(torch_cuda):
     """The 96-head prefill batch at full size (B=8 x 2048 tokens), in the
-    launch the benchmark times; the oracle checks 6 sampled tiles."""
+    launch the benchmark times: 128 sampled tiles (the grid's first and last
+    among them) against the oracle, and every slot outside state_indices
+    bit-identical."""
     cfg = wl.PRESETS[wl.PREFILL_HEADLINE]
     _say("prefill headline", cfg.description)
-    stats, _, _ = H.parity_case(wl.draw(cfg), entry="prefill", sample=6, check_untouched=False)
+    stats, _, _ = H.parity_case(wl.draw(cfg), entry="prefill", sample=126)
     print("prefill headline", stats, flush=True)
+    torch_cuda.cuda.empty_cache()
+
+
+def test_prefill_one_long_prompt_sampled(torch_cuda):
+    """One 16384-token prompt over 96 heads (the long-prompt bench batch),
+    in the launch the benchmark times: 8 sampled heads against the oracle."""
+    cfg = wl.PRESETS["prefill_b1_t16384_h96"]
+    _say("prefill one long prompt", cfg.description)
+    stats, _, _ = H.parity_case(wl.draw(cfg), entry="prefill", sample=6)
+    print("prefill long prompt", stats, flush=True)
     torch_cuda.cuda.empty_cache()
 
 
