@@ -34,9 +34,12 @@
 // part of its own channels.  For a channel set whose decay span
 // max(-Gamma_last[d]) is at most kSafeSpan, that part is one matrix product
 // of Kp = k exp(Gamma - c) and Ks = k exp(c - Gamma) with c = Gamma_last / 2:
-// every factor then lies within exp(+-kSafeSpan / 2), far from fp32 overflow
-// and from subnormals.  A wider span (a strong softplus gate) takes the
-// pair-by-pair sums, with exp(Gamma_t - Gamma_s) <= 1 formed per term.
+// every factor then lies within exp(+-kSafeSpan / 2) = exp(+-60): finite for
+// any |k| below 1e12, and the bf16 remainder of the smallest factor is a
+// normal number for any |k| above 1e-9.  A wider span (a strong softplus gate) splits the
+// chunk's lower triangle hierarchically into blocks that each factor with
+// every exponent bounded (see wide_level): two to five products instead of
+// one, for any decay span.
 //
 // Work decomposition.  A workgroup owns one (request, value head) tile and
 // walks the request's chunks in order; wave w owns value columns
@@ -94,16 +97,16 @@ namespace {
 constexpr int kChunk = 16;          // tokens per chunk: one MFMA M / K tile
 constexpr int kSlabCols = 32;       // value columns per wave (two MFMA N tiles)
 constexpr int kGroupChannels = 32;  // key channels per elementwise channel group
-constexpr float kSafeSpan = 80.0f;  // largest decay span of the one-product P, R
-// Pair-by-pair exponents Gamma_t - Gamma_s are differences of prefix sums;
-// in fp32 they carry an error near ulp(|Gamma|), harmless while a chunk's
-// decay span stays within kExactSpan (in log2 units; ulp(512) = 2^-14 gives
-// factor errors of order 1e-5).  A wider span, or a non-finite one, splits
-// each token's log2-decay g into an integer, whose prefix sums are exact in
-// fp32, and a remainder in (-1, 0], whose prefix sums stay within 16
-// (ulp 2^-20); g is first raised to -kGateFloor (exp2 of it is already 0 in
-// fp32), which keeps an infinite decay finite and the integer sums below
-// 2^24.
+constexpr float kSafeSpan = 120.0f; // largest decay span of the one-product P, R
+// The table factors exp(Gamma_t) and exp(Gamma_last - Gamma_t) use
+// differences of prefix sums; in fp32 they carry an error near
+// ulp(|Gamma|), harmless while a chunk's decay span stays within kExactSpan
+// (in log2 units; ulp(512) = 2^-14 gives factor errors of order 1e-5).  A
+// wider span, or a non-finite one, splits each token's log2-decay g into an
+// integer, whose prefix sums are exact in fp32, and a remainder in (-1, 0],
+// whose prefix sums stay within 16 (ulp 2^-20); g is first raised to
+// -kGateFloor (exp2 of it is already 0 in fp32), which keeps an infinite
+// decay finite and the integer sums below 2^24.
 constexpr float kExactSpan = 512.0f;
 constexpr float kGateStep = 1.0f;
 constexpr float kGateFloor = 1048576.0f;   // 2^20
@@ -347,9 +350,9 @@ struct RowTable<KDA_MATMUL_SPLIT_BF16, DK> {
 
 // Kup_raw^T [channel][token] in LDS, written one value at a time by the
 // lane that owns (token, channel) and read as K = 16 fragments of four
-// consecutive tokens.  The split form packs hi (upper half) and lo (lower
-// half) of one value into a word; a fragment is reassembled with byte
-// permutes instead of being split again by every wave.
+// consecutive tokens.  The split form keeps, per channel and group of four
+// tokens, the four hi parts and then the four lo parts: one 16-byte read is
+// the fragment as the matrix instruction takes it.
 template <int PREC, int DK>
 struct KupTable;
 
@@ -364,20 +367,18 @@ struct KupTable<KDA_MATMUL_F32, DK> {
 
 template <int DK>
 struct KupTable<KDA_MATMUL_SPLIT_BF16, DK> {
-  uint32_t v[DK][kPT];
+  static constexpr int P = kChunk / 4 * 8 + 8;   // bf16 per channel row, padded
+  __bf16 v[DK][P];
   __device__ __forceinline__ void store(int d, int t, float x) {
     const bf16x2 h = {static_cast<__bf16>(x), static_cast<__bf16>(x)};
-    const bf16x2 w = {static_cast<__bf16>(minus_hi(h, 1, x)), h[1]};
-    v[d][t] = __builtin_bit_cast(uint32_t, w);
+    v[d][8 * (t / 4) + t % 4] = h[1];
+    v[d][8 * (t / 4) + 4 + t % 4] = static_cast<__bf16>(minus_hi(h, 1, x));
   }
   __device__ __forceinline__ Frag<KDA_MATMUL_SPLIT_BF16, 4> frag4(int row, int g) const {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(&v[row][4 * g]);
-    constexpr uint32_t kUpper = 0x07060302u, kLower = 0x05040100u;
-    const u32x2 hi = {__builtin_amdgcn_perm(w[1], w[0], kUpper), __builtin_amdgcn_perm(w[3], w[2], kUpper)};
-    const u32x2 lo = {__builtin_amdgcn_perm(w[1], w[0], kLower), __builtin_amdgcn_perm(w[3], w[2], kLower)};
+    const bf16x8 w = *reinterpret_cast<const bf16x8*>(&v[row][8 * g]);
     Frag<KDA_MATMUL_SPLIT_BF16, 4> f;
-    f.hi = __builtin_bit_cast(bf16x4, hi);
-    f.lo = __builtin_bit_cast(bf16x4, lo);
+    f.hi = __builtin_shufflevector(w, w, 0, 1, 2, 3);
+    f.lo = __builtin_shufflevector(w, w, 4, 5, 6, 7);
     return f;
   }
 };
@@ -518,14 +519,16 @@ __device__ __forceinline__ float cross_row_sum(float x) {
   return swap32_add(x, x);
 }
 
-// Steps S.. of the row substitution for T = (I + L)^-1: lane (t, g) holds
-// T[t][4g + j] in t4 and -L[t][s] in nlt[s].  Row 15 updates nothing.
-template <int S>
-__device__ __forceinline__ void solve_rows(f32x4& t4, const float (&nlt)[kChunk]) {
+// Steps S.. of the row substitution for J columns of T = (I + L)^-1: lane
+// (t, g) holds T[t][c_j] in tc[j], with column c_j the same for the 16
+// lanes of its row, and -L[t][s] in nlt[s].  At step s row s is final and
+// reaches its row's lanes by one broadcast.  Row 15 updates nothing.
+template <int S, int J>
+__device__ __forceinline__ void solve_rows(float (&tc)[J], const float (&nlt)[kChunk]) {
   if constexpr (S < kChunk - 1) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) t4[j] = fmaf(nlt[S], dpp_row<kDppRowBcast0 + S, true>(t4[j]), t4[j]);
-    solve_rows<S + 1>(t4, nlt);
+    for (int j = 0; j < J; ++j) tc[j] = fmaf(nlt[S], dpp_row<kDppRowBcast0 + S, true>(tc[j]), tc[j]);
+    solve_rows<S + 1, J>(tc, nlt);
   }
 }
 
@@ -546,12 +549,15 @@ struct alignas(16) ChunkShared {
   float nk[kChunk][NWP];
   float pp[NW][kChunk][kPT];      // P_raw partial of wave w, transposed: [s][t]
   float rr[NW][kChunk][kPT];      // R_raw partial of wave w: [t][s]
-  // private to each wave
-  float nl[NW][kChunk][kPT];      // -L: [t][s]
-  float pq[NW][kChunk][kGroupChannels + 4];   // raw q, k and Gamma of the wave's
-  float pk[NW][kChunk][kGroupChannels + 4];   //   channel group, for the pair-by-
-  float pg[NW][kChunk][kGroupChannels + 4];   //   pair P and R (Gamma as its exact
-  float ps[NW][kChunk][kGroupChannels + 4];   //   integer parts and remainders)
+  // Used either before the first barrier of a chunk (the exact decay sums)
+  // or between that barrier and the last (-L), never both.
+  union {
+    struct {                      // private to each wave: the exact decay sums
+      float pg[NW][kChunk][kGroupChannels + 4];   // of its channel group (prefix
+      float ps[NW][kChunk][kGroupChannels + 4];   // sums of integer parts, of remainders)
+    };
+    float nl[NW][kChunk][kPT];    // -L: [t][s], each wave its own copy
+  };
 };
 
 // Raw inputs of one chunk for one lane: per channel group pass, q, k and
@@ -574,13 +580,21 @@ struct ChunkInputs {
 // Per-token log2-decays of N channels, log2(e) g: the softplus form
 // -exp(A_log) softplus(x + dt_bias), or the lower-bound form
 // lb sigmoid(exp(A_log) (x + dt_bias)) = lb / (1 + exp(-z)) with
-// exp(-z) = exp2(-z log2(e)); zero for a padding token.
+// exp(-z) = exp2(-z log2(e)); zero for a padding token.  The softplus is
+// taken in base 2, log2(e) softplus(z) = log2(e) max(z, 0) +
+// log2(1 + 2^(-|z| log2(e))): the decay factor exp(g) only sees the
+// absolute error of g, which here is about exp(A_log) * 1e-7 (the rounding
+// of 1 + 2^(...)) at most, as for the softplus with the corrected log1p.
 template <int N>
-__device__ __forceinline__ void log2_decays(int gate_mode, float amp2, float lb2, bool live,
+__device__ __forceinline__ void log2_decays(int gate_mode, float amp, float amp2, float lb2, bool live,
                                             const float (&x)[N], const float (&dtb)[N], float (&G)[N]) {
   if (gate_mode == KDA_GATE_SOFTPLUS) {     // uniform branch
 #pragma unroll
-    for (int j = 0; j < N; ++j) G[j] = -amp2 * softplus_f(x[j] + dtb[j]);
+    for (int j = 0; j < N; ++j) {
+      const float z = x[j] + dtb[j];
+      const float l = __builtin_amdgcn_logf(1.0f + exp2_f(-kLog2e * fabsf(z)));   // log2
+      G[j] = -fmaf(amp2, fmaxf(z, 0.0f), amp * l);
+    }
   } else {
 #pragma unroll
     for (int j = 0; j < N; ++j) G[j] = lb2 * __builtin_amdgcn_rcpf(1.0f + exp2_f(-amp2 * (x[j] + dtb[j])));
@@ -589,37 +603,133 @@ __device__ __forceinline__ void log2_decays(int gate_mode, float amp2, float lb2
   for (int j = 0; j < N; ++j) G[j] = live ? G[j] : 0.0f;
 }
 
-// The pair-by-pair parts of P_raw and R_raw^T over one wave's channel
-// group: lane pairs (t, s), s <= t, four per lane.  The table rows hold raw
-// q and k and Gamma, the latter as one prefix sum or (EXACT) as the exact
-// sums of integer parts in pg and of the remainders in ps.
-template <bool EXACT, class Shared>
-__device__ __forceinline__ void pair_sums(const Shared& sh, int w, int lane, float (&pw)[4], float (&rw)[4]) {
+// ---------------------------------------------------------------------------
+// wide decay spans: hierarchical factoring of P and R
+// ---------------------------------------------------------------------------
+//
+// For a chunk whose decay span is too wide for the one-product form, the
+// lower triangle of P (and R) is split hierarchically.  Within every
+// aligned block of 2h tokens (h = 8, 4, 2, 1), a pair t in the upper half
+// and s in the lower half factors through the lower half's last token r:
+// exp(Gamma_t - Gamma_s) = exp(Gamma_t - Gamma_r) exp(Gamma_r - Gamma_s),
+// where the first exponent is the sum of the gates of t's half up to t
+// (inclusive) and the second that of s's half after s: both factors are at
+// most 1, and each exponent is a sum inside one half (a segmented scan over
+// the lanes), so no large prefix cancels and an infinite decay only gives
+// zeros.  One product per level covers all its pairs; its other entries are
+// discarded.  The pairs left, inside the diagonal blocks of b = 16 >> tier
+// tokens, take the midpoint factoring of their own block (exponents within
+// +-span/2, which the tier choice bounds), or at b = 1 the plain diagonal
+// sum.  The tier is the smallest whose diagonal blocks all span at most
+// kSafeSpan, per wave (its own channel group).
+
+constexpr int kDppQuad0000 = 0x00;   // quad_perm [0,0,0,0]
+constexpr int kDppQuad0022 = 0xA0;   // quad_perm [0,0,2,2]
+constexpr int kDppQuad1111 = 0x55;   // quad_perm [1,1,1,1]
+constexpr int kDppQuad1133 = 0xF5;   // quad_perm [1,1,3,3]
+constexpr int kDppQuad2222 = 0xAA;   // quad_perm [2,2,2,2]
+constexpr int kDppQuad3333 = 0xFF;   // quad_perm [3,3,3,3]
+constexpr int kDppRowShl1 = 0x101;
+constexpr int kDppRowShl4 = 0x104;
+
+// Every cross-lane move below runs on all lanes and only then is selected:
+// written as `cond ? move(x) : 0` the compiler may issue the move under a
+// partial exec mask, and a move that reads a disabled lane gets no value.
+
+// Inclusive sums of x over the aligned blocks of 2, 4 and 8 lanes of each
+// 16-lane row (lane n = token).
+__device__ __forceinline__ void seg_prefix(float x, int n, float& f2, float& f4, float& f8) {
+  const float y1 = dpp_row<kDppQuad0022, false>(x);
+  f2 = x + ((n & 1) ? y1 : 0.0f);
+  const float y2 = dpp_row<kDppQuad1111, false>(f2);
+  f4 = f2 + ((n & 2) ? y2 : 0.0f);
+  const float y4 = dpp_row<kDppRowShr4, true>(dpp_row<kDppQuad3333, false>(f4));
+  f8 = f4 + ((n & 4) ? y4 : 0.0f);
+}
+
+// One step of the inclusive suffix sums within aligned blocks: from blocks
+// of H / 2 lanes to blocks of H (H = 2, 4, 8).
+template <int H>
+__device__ __forceinline__ float seg_suffix_step(float r, int n) {
+  float y;
+  if constexpr (H == 2) y = dpp_row<kDppQuad1133, false>(r);
+  else if constexpr (H == 4) y = dpp_row<kDppQuad2222, false>(r);
+  else y = dpp_row<kDppRowShl4, true>(dpp_row<kDppQuad0000, false>(r));
+  return r + ((n & (H / 2)) ? 0.0f : y);
+}
+
+// The entry (t, s) of a P or R^T accumulator element i at lane (n, g):
+// t ^ s = (4g + i) ^ n in both layouts.
+__device__ __forceinline__ int pair_xor(int n, int g, int i) { return (4 * g + i) ^ n; }
+
+// Diagonal blocks of B tokens (B = 8, 4, 2): fb holds the inclusive sums of
+// the log2-decays within each block; every factor lies within 2^(+-span/2).
+template <int B, int PREC, int CPL>
+__device__ __forceinline__ void wide_diagonal(f32x4& Pw, f32x4& Rw, const float (&fb)[CPL],
+                                              const float (&k)[CPL], const float (&q)[CPL], int n, int g) {
+  float kp[CPL], qp[CPL], ks[CPL];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int pi = lane + 64 * r;
-    const int tt = pi / kChunk, ss = pi % kChunk;
-    if (ss <= tt) {
-      float pv = 0.0f, rv = 0.0f;
-      for (int d = 0; d < kGroupChannels; d += 4) {
-        const f32x4 kt4 = *reinterpret_cast<const f32x4*>(&sh.pk[w][tt][d]);
-        const f32x4 qt4 = *reinterpret_cast<const f32x4*>(&sh.pq[w][tt][d]);
-        const f32x4 ks4 = *reinterpret_cast<const f32x4*>(&sh.pk[w][ss][d]);
-        f32x4 dg = *reinterpret_cast<const f32x4*>(&sh.pg[w][tt][d]) -
-                   *reinterpret_cast<const f32x4*>(&sh.pg[w][ss][d]);   // Gamma_t - Gamma_s
-        if constexpr (EXACT)
-          dg += *reinterpret_cast<const f32x4*>(&sh.ps[w][tt][d]) -
-                *reinterpret_cast<const f32x4*>(&sh.ps[w][ss][d]);
+  for (int j = 0; j < CPL; ++j) {
+    float end;   // the block's total: the sum at its last lane
+    if constexpr (B == 8) {
+      const float e15 = dpp_row<kDppRowBcast15, true>(fb[j]);
+      const float e7 = dpp_row<kDppRowBcast0 + 7, true>(fb[j]);
+      end = (n & 8) ? e15 : e7;
+    } else if constexpr (B == 4) end = dpp_row<kDppQuad3333, false>(fb[j]);
+    else end = dpp_row<kDppQuad1133, false>(fb[j]);
+    const float ep = exp2_f(fmaf(-0.5f, end, fb[j]));
+    kp[j] = k[j] * ep;
+    qp[j] = q[j] * ep;
+    ks[j] = k[j] * __builtin_amdgcn_rcpf(ep);
+  }
+  f32x4 Pd = {0.0f, 0.0f, 0.0f, 0.0f}, Rd = {0.0f, 0.0f, 0.0f, 0.0f};
+  mma(Pd, make_frag<PREC, CPL>(kp), make_frag<PREC, CPL>(ks));
+  mma(Rd, make_frag<PREC, CPL>(ks), make_frag<PREC, CPL>(qp));
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float e = ks4[j] * exp2_f(fminf(dg[j], 0.0f));
-          pv = fmaf(kt4[j], e, pv);
-          rv = fmaf(qt4[j], e, rv);
-        }
-      }
-      pw[r] += pv;
-      rw[r] += rv;
-    }
+  for (int i = 0; i < 4; ++i) {
+    const bool own = pair_xor(n, g, i) < B;
+    Pw[i] = own ? Pd[i] : Pw[i];
+    Rw[i] = own ? Rd[i] : Rw[i];
+  }
+}
+
+// The exclusive suffix sums within aligned blocks of H lanes (the gates
+// after s inside its block), from the inclusive ones rh.
+template <int H, int CPL>
+__device__ __forceinline__ void suffix_excl(float (&rx)[CPL], const float (&rh)[CPL], int n) {
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const float y = dpp_row<kDppRowShl1, true>(rh[j]);
+    rx[j] = ((n + 1) & (H - 1)) ? y : 0.0f;
+  }
+}
+
+// The level of half size H: fh holds the inclusive sums within aligned
+// blocks of H lanes, rx the exclusive suffix sums within them (the lower
+// half's exponents; zero at H = 1).
+template <int H, int PREC, int CPL>
+__device__ __forceinline__ void wide_level(f32x4& Pw, f32x4& Rw, const float (&fh)[CPL], const float (&rx)[CPL],
+                                           const float (&k)[CPL], const float (&q)[CPL], int n, int g) {
+  const bool up = (n & H) != 0;
+  float aP[CPL], aR[CPL], bK[CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const float f = exp2_f(up ? fh[j] : rx[j]);
+    const float kf = k[j] * f;
+    aP[j] = up ? kf : 0.0f;
+    aR[j] = up ? q[j] * f : 0.0f;
+    bK[j] = up ? 0.0f : kf;
+  }
+  f32x4 Pl = {0.0f, 0.0f, 0.0f, 0.0f}, Rl = {0.0f, 0.0f, 0.0f, 0.0f};
+  const Frag<PREC, CPL> fb = make_frag<PREC, CPL>(bK);
+  mma(Pl, make_frag<PREC, CPL>(aP), fb);
+  mma(Rl, fb, make_frag<PREC, CPL>(aR));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int x = pair_xor(n, g, i);
+    const bool own = x >= H && x < 2 * H;
+    Pw[i] = own ? Pl[i] : Pw[i];
+    Rw[i] = own ? Rl[i] : Rw[i];
   }
 }
 
@@ -760,8 +870,6 @@ kda_prefill_chunks(DecodeArgs a) {
     float sq = 0.0f, sk = 0.0f;
     f32x4 Pp = {0.0f, 0.0f, 0.0f, 0.0f};   // P_raw partial (acc: rows t, column s)
     f32x4 Rp = {0.0f, 0.0f, 0.0f, 0.0f};   // R_raw^T partial (acc: rows s, column t)
-    float pw[4] = {0.0f, 0.0f, 0.0f, 0.0f}, rw[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    bool any_wide = false;
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
       if (w + NW * p >= NG) continue;
@@ -779,7 +887,10 @@ kda_prefill_chunks(DecodeArgs a) {
         sk = fmaf(k[j], k[j], sk);
       }
       // G, GL: Gamma and Gamma_last of the lane's channels, times log2(e)
-      log2_decays<CPL>(a.gate_mode, amp2, lb2, live, x, dtb[p], G);
+      log2_decays<CPL>(a.gate_mode, amp, amp2, lb2, live, x, dtb[p], G);
+      float gr[CPL];   // the per-token log2-decays themselves, for wide spans
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) gr[j] = G[j];
       bool wide_lane = false;
 #pragma unroll
       for (int j = 0; j < CPL; ++j) {
@@ -811,11 +922,6 @@ kda_prefill_chunks(DecodeArgs a) {
           qt[j] = q[j] * eg;
           sh.kup.store(chan0[p] + j, n, last_real ? k[j] : k[j] * exp2_f(GL[j] - G[j]));
         }
-        if (wide) {
-#pragma unroll
-          for (int j = 0; j < CPL; j += 4)
-            *reinterpret_cast<f32x4*>(&sh.pg[w][n][CPL * g + j]) = f32x4{G[j], G[j + 1], G[j + 2], G[j + 3]};
-        }
       } else {
         // Gamma again, as Gb + Gs: Gb the prefix sums of the gates' integer
         // parts (exact), Gs those of the remainders (at most 16 in
@@ -831,7 +937,7 @@ kda_prefill_chunks(DecodeArgs a) {
           xr.load(a.raw_gate, (tok * a.HV + hv) * DK + chan0[p]);
           float xg[CPL], gg[CPL];
           xr.unpack(xg);
-          log2_decays<CPL>(a.gate_mode, amp2, lb2, live, xg, dtb[p], gg);
+          log2_decays<CPL>(a.gate_mode, amp, amp2, lb2, live, xg, dtb[p], gg);
 #pragma unroll
           for (int j = 0; j < CPL; j += 4)
             *reinterpret_cast<f32x4*>(&sh.pg[w][n][CPL * g + j]) = f32x4{gg[j], gg[j + 1], gg[j + 2], gg[j + 3]};
@@ -890,17 +996,67 @@ kda_prefill_chunks(DecodeArgs a) {
         mma(Pp, fkp, fks);    // P[t][s] = Kp[t] . Ks[s]
         mma(Rp, fks, fqp);    // R^T[s][t] = Ks[s] . Qp[t]
       } else {
-        // pair by pair through the wave's scratch rows
+        // hierarchical factoring (see wide_level): the tier from the spans
+        // of the aligned blocks of 8, 4 and 2 tokens.  The gates are <= 0,
+        // so a block's most negative partial sum is its total: the minimum
+        // over all lanes and channels is the widest block's span.
+        float f2[CPL], f4[CPL], f8[CPL];
+        float m8 = 0.0f, m4 = 0.0f, m2 = 0.0f;
 #pragma unroll
-        for (int j = 0; j < CPL; j += 4) {
-          *reinterpret_cast<f32x4*>(&sh.pq[w][n][CPL * g + j]) = f32x4{q[j], q[j + 1], q[j + 2], q[j + 3]};
-          *reinterpret_cast<f32x4*>(&sh.pk[w][n][CPL * g + j]) = f32x4{k[j], k[j + 1], k[j + 2], k[j + 3]};
+        for (int j = 0; j < CPL; ++j) {
+          seg_prefix(gr[j], n, f2[j], f4[j], f8[j]);
+          m8 = fminf(m8, f8[j]);
+          m4 = fminf(m4, f4[j]);
+          m2 = fminf(m2, f2[j]);
         }
-        wave_lds_order();
-        if (exact) pair_sums<true>(sh, w, lane, pw, rw);
-        else pair_sums<false>(sh, w, lane, pw, rw);
-        wave_lds_order();
-        any_wide = true;
+        constexpr float kSpan2 = kSafeSpan * kLog2e;
+        const int tier = !__any(!(-m8 <= kSpan2)) ? 1 : !__any(!(-m4 <= kSpan2)) ? 2
+                       : !__any(!(-m2 <= kSpan2)) ? 3 : 4;
+        f32x4 Pw = {0.0f, 0.0f, 0.0f, 0.0f}, Rw = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (tier == 1) {
+          // the common wide case: the halves' spans are bounded, so the
+          // lower half's exponents may be taken as differences of its
+          // prefix sums (no larger than the tier-0 exponents)
+          wide_diagonal<8, PREC>(Pw, Rw, f8, k, q, n, g);
+          float rx[CPL];
+#pragma unroll
+          for (int j = 0; j < CPL; ++j) rx[j] = dpp_row<kDppRowBcast0 + 7, true>(f8[j]) - f8[j];
+          wide_level<8, PREC>(Pw, Rw, f8, rx, k, q, n, g);
+        } else {
+          if (tier == 2) wide_diagonal<4, PREC>(Pw, Rw, f4, k, q, n, g);
+          else if (tier == 3) wide_diagonal<2, PREC>(Pw, Rw, f2, k, q, n, g);
+          else {   // blocks of one token: R's diagonal is q_t . k_t (P's is unused)
+            float qk = 0.0f;
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) qk = fmaf(q[j], k[j], qk);
+            qk = cross_row_sum(qk);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Rw[i] = pair_xor(n, g, i) == 0 ? qk : 0.0f;
+          }
+          // the lower halves' exponents from suffix sums within blocks of
+          // 1, 2, 4, 8 in turn (exact for any span)
+          float rs[CPL], rx[CPL];
+#pragma unroll
+          for (int j = 0; j < CPL; ++j) {
+            rs[j] = seg_suffix_step<2>(gr[j], n);
+            rx[j] = 0.0f;
+          }
+          if (tier >= 4) wide_level<1, PREC>(Pw, Rw, gr, rx, k, q, n, g);
+          if (tier >= 3) {
+            suffix_excl<2>(rx, rs, n);
+            wide_level<2, PREC>(Pw, Rw, f2, rx, k, q, n, g);
+          }
+#pragma unroll
+          for (int j = 0; j < CPL; ++j) rs[j] = seg_suffix_step<4>(rs[j], n);
+          suffix_excl<4>(rx, rs, n);
+          wide_level<4, PREC>(Pw, Rw, f4, rx, k, q, n, g);
+#pragma unroll
+          for (int j = 0; j < CPL; ++j) rs[j] = seg_suffix_step<8>(rs[j], n);
+          suffix_excl<8>(rx, rs, n);
+          wide_level<8, PREC>(Pw, Rw, f8, rx, k, q, n, g);
+        }
+        Pp += Pw;
+        Rp += Rw;
       }
     }
     // publish the partials
@@ -913,18 +1069,6 @@ kda_prefill_chunks(DecodeArgs a) {
     }
     *reinterpret_cast<f32x4*>(&sh.pp[w][n][4 * g]) = Pp;   // pp[s = n][t = 4g + i]
     *reinterpret_cast<f32x4*>(&sh.rr[w][n][4 * g]) = Rp;   // rr[t = n][s = 4g + i]
-    if (any_wide) {
-      wave_lds_order();
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int pi = lane + 64 * r;
-        const int tt = pi / kChunk, ss = pi % kChunk;
-        if (ss <= tt) {
-          sh.pp[w][ss][tt] += pw[r];
-          sh.rr[w][tt][ss] += rw[r];
-        }
-      }
-    }
     lds_barrier();
 
     // ================= per wave: norms, L, T, then the slab's products
@@ -972,10 +1116,11 @@ kda_prefill_chunks(DecodeArgs a) {
     wave_lds_order();
     // T = (I + L)^-1 with lane (t = n, g) holding T[t][4g + j], the A operand
     // of T X: forward substitution over the rows, T[t][.] -= L[t][s] T[s][.]
-    // for s = 0, 1, ...; row s is final at step s and reaches every lane of
-    // its 16-lane row by DPP broadcast.  L is zero on and above the
-    // diagonal, so the update leaves rows t <= s unchanged.
-    f32x4 t4;
+    // for s = 0, 1, ...; L is zero on and above the diagonal, so the update
+    // leaves rows t <= s unchanged.  (Every wave solves the whole of T: with
+    // each wave solving a quarter of the columns and the quarters exchanged
+    // through LDS, the extra barrier cost more than the saved instructions.)
+    float tc[4];
     {
       float nlt[kChunk];
 #pragma unroll
@@ -985,19 +1130,17 @@ kda_prefill_chunks(DecodeArgs a) {
         for (int j = 0; j < 4; ++j) nlt[4 * q4 + j] = l4[j];
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) t4[j] = n == 4 * g + j ? 1.0f : 0.0f;
-      solve_rows<0>(t4, nlt);
+      for (int j = 0; j < 4; ++j) tc[j] = n == 4 * g + j ? 1.0f : 0.0f;
+      solve_rows<0, 4>(tc, nlt);
     }
     // R_raw as the B operand of R_raw^T: lane (t = n, g) holds R[t][4g + j]
-    Frag<PREC, 4> fr;
+    float rv[4];
     {
       f32x4 Rf = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int ww = 0; ww < NW; ++ww) Rf += *reinterpret_cast<const f32x4*>(&sh.rr[ww][n][4 * g]);
-      float rv[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) rv[j] = 4 * g + j <= n ? Rf[j] : 0.0f;
-      fr = make_frag<PREC, 4>(rv);
     }
 
     // X = V - diag(rk) Kt_raw S,  Y^T = S^T Qt_raw^T   (per value tile nt)
@@ -1029,8 +1172,11 @@ kda_prefill_chunks(DecodeArgs a) {
     }
 
     // U = T X, U' = diag(beta rk) U, O^T = diag(rq)(Y^T + U'^T R_raw^T),
-    // S = diag(exp(Gamma_last)) S + Kup_raw^T U'
-    const Frag<PREC, 4> ft = acc_frag4<PREC>(t4);
+    // S = diag(exp(Gamma_last)) S + Kup_raw^T U'.  (The K = 16 products of
+    // the chunk's own tokens stay in the matrix precision: on the fp32
+    // instruction, whose operands need no split, they measured slower.)
+    const Frag<PREC, 4> ft = make_frag<PREC, 4>(tc);
+    const Frag<PREC, 4> fr = make_frag<PREC, 4>(rv);
     Frag<PREC, 4> fu[NTV];
 #pragma unroll
     for (int nt = 0; nt < NTV; ++nt) {

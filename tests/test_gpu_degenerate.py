@@ -98,18 +98,28 @@ def test_prefill_degenerate_finite_gates(torch_cuda, matmul):
     print(stats, flush=True)
 
 
-@pytest.mark.parametrize("matmul", ["split_bf16", "f32"])
-@pytest.mark.parametrize("shift", [4.0, 8.0, 30.0])
-def test_prefill_strong_softplus_gates(torch_cuda, matmul, shift):
-    """Strong but ordinary decays: every gate pre-activation shifted up, so
-    each token decays by about amp * shift nats and the chunk spans of this
-    batch run from about 200 to about 11 000 (log2 units), across the
-    single-prefix and the split-prefix pair paths."""
+STRONG_SHIFTS = (4.0, 8.0, 30.0)
+
+
+def strong_softplus_inputs(shift):
+    """The strong-gate batch: every softplus pre-activation shifted up by
+    ``shift``."""
     cfg = wl.Workload(name="strong_softplus", B=3, H=2, HV=4, DK=128, DV=128, n_slots=7,
                       cu_seqlens=(0, 37, 70, 118), qkv_dtype="bf16", gate_mode=wl.SOFTPLUS,
                       seed=12, host_state=True, state_layout="v_first")
-    _say("prefill strong softplus", matmul, shift)
     inp = wl.draw(cfg)
     inp.raw_gate += np.float32(shift)
+    return inp
+
+
+@pytest.mark.parametrize("matmul", ["split_bf16", "f32"])
+@pytest.mark.parametrize("shift", STRONG_SHIFTS)
+def test_prefill_strong_softplus_gates(torch_cuda, matmul, shift):
+    """Strong but ordinary decays: every gate pre-activation shifted up, so
+    each token decays by about amp * shift nats and the chunk spans of this
+    batch run from about 200 to about 11 000 (log2 units): the wide-span
+    tiers of P and R, and the split prefix sums of the tables."""
+    _say("prefill strong softplus", matmul, shift)
+    inp = strong_softplus_inputs(shift)
     stats, _, _ = H.parity_case(inp, entry="prefill", matmul=matmul)
     print(stats, flush=True)
