@@ -25,8 +25,9 @@ the dense bf16 peak; or once over the fp32 matrix peak).
 Fields beyond the common ones:
   roofline      roofline of the dominant kernel: achieved = algorithmic
                 bytes per launch (state read + write of every active tile,
-                plus every token tensor once) / mean kernel time measured
-                with HIP events on the launch stream; peak 8000 GB/s;
+                plus every token tensor once) / mean launch duration (one
+                pair of HIP events on the launch stream around the K timed
+                launches, divided by K); peak 8000 GB/s;
                 traffic = HBM bytes per launch from the committed rocprofv3
                 FETCH_SIZE / WRITE_SIZE summary (null when the kernel source
                 changed since the counters were taken).
@@ -360,50 +361,66 @@ def main(argv=None) -> int:
     handle = stream.cuda_stream
     mode = dict(gate_mode=cfg.gate_mode, lower_bound=cfg.lower_bound, state_layout=cfg.state_layout)
 
+    # The C ABI is called with descriptors built once per slot set, so that
+    # the host enqueues a launch in a few microseconds and the GPU never
+    # waits for the next one (the short batches' kernels take ~50 us).
+    kmode = kda.make_mode(**mode)
+    desc = lambda t, nm: kda._descriptor(t, nm)   # noqa: E731
     if args.conv:
         ci = wl.draw_conv(inp)
         cd = wl.conv_to_device(ci, cfg.qkv_dtype)
         conv_bytes = wl.conv_bytes(cfg, inp, ci.K)
         alg_bytes += conv_bytes
         torch.cuda.synchronize()
+        conv = kda.KdaConv(*[desc(cd[n], n) for n in kda.CONV_FIELDS])
+        out_d = desc(out, "out")
+        tensors = dict(dev, state_pool=pool)
+        rests = [[desc(ix, n) if n == "state_indices" else desc(tensors[n], n) for n in kda.CONV_REST]
+                 for ix in idx_sets]
 
         def step(i):
-            kda.decode_conv(out, cd["x_q"], cd["x_k"], cd["x_v"], cd["w_q"], cd["w_k"], cd["w_v"],
-                            cd["win_q"], cd["win_k"], cd["win_v"], cd["q_conv"], cd["k_conv"],
-                            dev["raw_gate"], dev["beta_logits"], dev["a_log"], dev["dt_bias"],
-                            dev["cu_seqlens"], pool, idx_sets[i % len(idx_sets)], stream=handle,
-                            **mode)
-    elif args.prefill:
-        def step(i):
-            kda.prefill(out, dev["q"], dev["k"], dev["v"], dev["raw_gate"], dev["beta_logits"],
-                        dev["a_log"], dev["dt_bias"], dev["cu_seqlens"], pool,
-                        idx_sets[i % len(idx_sets)], stream=handle, matmul=args.matmul, **mode)
+            rc = kda.call_raw_conv(out_d, conv, rests[i % len(rests)], kmode, handle)
+            if rc != kda.KDA_OK:
+                raise kda.KdaError(rc, "kda_decode_conv")
     else:
-        def step(i):
-            kda.decode(out, dev["q"], dev["k"], dev["v"], dev["raw_gate"], dev["beta_logits"],
-                       dev["a_log"], dev["dt_bias"], dev["cu_seqlens"], pool,
-                       idx_sets[i % len(idx_sets)], stream=handle, **mode)
+        tensors = dict(dev, out=out, state_pool=pool)
+        descs = [[desc(ix, n) if n == "state_indices" else desc(tensors[n], n) for n in kda.ARG_NAMES]
+                 for ix in idx_sets]
+        if args.prefill:
+            mm = kda.MATMULS[args.matmul]
+
+            def step(i):
+                rc = kda.call_raw_prefill(descs[i % len(descs)], kmode, mm, handle)
+                if rc != kda.KDA_OK:
+                    raise kda.KdaError(rc, "kda_prefill")
+        else:
+            def step(i):
+                rc = kda.call_raw(descs[i % len(descs)], kmode, handle)
+                if rc != kda.KDA_OK:
+                    raise kda.KdaError(rc)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} done; timing {args.steps} steps")
 
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # One pair of HIP events on the launch stream brackets the K back-to-back
+    # launches: the mean launch duration is their span / K (events around
+    # every launch would add their own latency to each, several us on the
+    # short batches).
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    start.record(stream)
     for i in range(args.steps):
-        starts[i].record(stream)
         step(args.warmup + i)
-        ends[i].record(stream)
+    end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kernel_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
     ms_per_step = wall * 1e3 / args.steps
-    mean_kernel_ms = float(kernel_ms.mean())
+    mean_kernel_ms = start.elapsed_time(end) / args.steps
     log(f"[bench] wall {ms_per_step * 1e3:.1f} us/step, kernel mean {mean_kernel_ms * 1e3:.1f} us "
-        f"(min {kernel_ms.min() * 1e3:.1f}, max {kernel_ms.max() * 1e3:.1f})")
+        f"(HIP events around all {args.steps} launches)")
     del dev, out
     torch.cuda.empty_cache()
 
