@@ -164,6 +164,13 @@ __device__ __forceinline__ void store_scalar(void* base, int64_t off, float x) {
   else static_cast<float*>(base)[off] = x;
 }
 
+// Two consecutive values at an even element offset.
+template <bool BF16>
+__device__ __forceinline__ void store_pair(void* base, int64_t off, float x0, float x1) {
+  if constexpr (BF16) *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(base) + off) = f32x2_to_bf16x2_rne(x0, x1);
+  else *reinterpret_cast<float2*>(static_cast<float*>(base) + off) = make_float2(x0, x1);
+}
+
 // ---------------------------------------------------------------------------
 // the pieces both layouts share
 // ---------------------------------------------------------------------------
@@ -375,14 +382,15 @@ __device__ __forceinline__ float xchg_level(bool up, float lo, float hi) {
 }
 
 // HALF-sized transpose levels on lane bits BIT, BIT-1, ...: each level keeps
-// half of the values a lane carries and sums it with the partner's copy, so
-// the last level leaves one value per lane.
-template <int HALF, int BIT>
+// half of the values a lane carries and sums it with the partner's copy;
+// after LEVELS levels (by default until one value is left) a lane carries
+// HALF * 2 / 2^LEVELS values.
+template <int HALF, int BIT, int LEVELS = 32>
 __device__ __forceinline__ void transpose_levels(float* vals, int lane) {
   const bool up = ((lane >> BIT) & 1) != 0;
 #pragma unroll
   for (int m = 0; m < HALF; ++m) vals[m] = xchg_level<BIT>(up, vals[m], vals[m + HALF]);
-  if constexpr (HALF > 1) transpose_levels<HALF / 2, BIT - 1>(vals, lane);
+  if constexpr (HALF > 1 && LEVELS > 1) transpose_levels<HALF / 2, BIT - 1, LEVELS - 1>(vals, lane);
 }
 
 // Plain sums over lane bits HI down to LO (none when HI < LO).
@@ -400,9 +408,9 @@ __device__ __forceinline__ float sum_levels(float x) {
 // key-first layout: state [dk][dv]
 // ---------------------------------------------------------------------------
 
-template <int DK, int DV, bool QBF16, bool SBF16, bool CONVV>
+template <int DK, int DV, bool QBF16, bool SBF16, bool CONVV, int CWT = 32>
 __global__ __launch_bounds__(kWave) void kda_decode_kfirst(const DecodeArgs a) {
-  constexpr int CW = DV < 32 ? DV : 32;   // value columns of the wave's slab
+  constexpr int CW = DV < CWT ? DV : CWT;   // value columns of the wave's slab
   constexpr int SLABS = DV / CW;
   // values per lane and key row: 8 bf16 (one 16-byte access) for a bf16
   // pool when dk has a row for each of the 64 / (CW / 8) row groups, else 4
@@ -414,13 +422,20 @@ __global__ __launch_bounds__(kWave) void kda_decode_kfirst(const DecodeArgs a) {
   constexpr int LOG_CQ = log2_exact<CQ>();
   constexpr int LOG_RS = log2_exact<RS>();
   constexpr int LOG_NV = log2_exact<NV>();
+  // With more partial sums than row groups (a 64-column bf16 slab: 16 sums,
+  // 8 row groups) the transpose-reduce runs over every row-group bit and
+  // leaves NVL fully reduced sums per lane, lane rs holding sums
+  // rs * NVL .. rs * NVL + NVL - 1 (a for NVL consecutive columns, or b).
+  constexpr int NVL = LOG_NV > LOG_RS ? NV / RS : 1;
   constexpr int CPL = DK >= 2 * kWave ? DK / kWave : 1;   // setup channels per lane
-  static_assert(DK % RS == 0 && R >= 1 && LOG_NV <= LOG_RS, "tile shape");
+  static_assert(DK % RS == 0 && R >= 1, "tile shape");
+  static_assert(NVL == 1 || (NVL == 2 && !CONVV), "two sums per lane only without the v convolution");
   static_assert(CPL * kWave >= DK && CPL <= 2, "setup split");
-  // A bf16 slab row is 64 bytes, half a cache line shared with the next
-  // slab's wave: ordinary cached accesses let L2 merge the two halves
-  // (measured 341 us against 382 us with the nontemporal hint on the
-  // 96-head decode).  Full-line fp32 rows stream best with the hint.
+  // A 32-column bf16 slab row is 64 bytes, half a cache line shared with
+  // the next slab's wave: ordinary cached accesses let L2 merge the two
+  // halves (measured 341 us against 382 us with the nontemporal hint on the
+  // 96-head decode).  Full-line rows (fp32, or 64 bf16 columns) stream best
+  // with the hint.
   using IO = StateIO<SBF16, EPL, (SBF16 && CW * 2 < 128) ? 0 : kCachePolicyNT>;
 
   __shared__ __attribute__((aligned(16))) float2 red_tab[2][DK];
@@ -456,11 +471,12 @@ __global__ __launch_bounds__(kWave) void kda_decode_kfirst(const DecodeArgs a) {
 #pragma unroll
   for (int i = 0; i < R; ++i) IO::load(res, voff, i * kRowStep, S[i]);
 
-  // After the reduction lane rs holds value m = rs & (NV-1): a[col0 + m] when
-  // m < EPL, else b[col0 + m - EPL]; row groups rs >= NV carry duplicates.
-  const int m_final = rs & (NV - 1);
+  // After the reduction lane rs holds values m = m_final .. m_final + NVL - 1
+  // (m_final = rs & (NV-1), or rs * NVL): a[col0 + m] when m < EPL, else
+  // b[col0 + m - EPL]; row groups rs >= NV carry duplicates.
+  const int m_final = NVL == 1 ? (rs & (NV - 1)) : rs * NVL;
   const bool holds_a = m_final < EPL;
-  const bool owner = rs < NV;
+  const bool owner = NVL > 1 || rs < NV;
   const int my_col = col0 + (m_final & (EPL - 1));
 
   // with the convolution in front, the a-lanes convolve their v channel
@@ -471,9 +487,15 @@ __global__ __launch_bounds__(kWave) void kda_decode_kfirst(const DecodeArgs a) {
 
   int buf = 0;
   for (int t = j.t0; t < j.t1; ++t, buf ^= 1) {
-    float v_mine = holds_a ? load_scalar<QBF16>(a.v, static_cast<int64_t>(t) * a.HV * DV + v_ch) : 0.0f;
-    if constexpr (CONVV)
-      if (holds_a) v_mine = cv.step(v_mine, a.conv_k);
+    float v_mine[NVL];
+    if constexpr (NVL == 1) {
+      v_mine[0] = holds_a ? load_scalar<QBF16>(a.v, static_cast<int64_t>(t) * a.HV * DV + v_ch) : 0.0f;
+      if constexpr (CONVV)
+        if (holds_a) v_mine[0] = cv.step(v_mine[0], a.conv_k);
+    } else {
+      v_mine[0] = v_mine[1] = 0.0f;
+      if (holds_a) load_qk<QBF16, 2>(a.v, static_cast<int64_t>(t) * a.HV * DV + v_ch, v_mine);
+    }
     // with the convolution in front, q and k arrive convolved in fp32
     const TokenScalars ts = token_setup<DK, CPL, QBF16 && !CONVV>(a, j, t, c0, chan_lane, dtb, amp,
                                                                 red_tab[buf], upd_tab[buf]);
@@ -494,11 +516,21 @@ __global__ __launch_bounds__(kWave) void kda_decode_kfirst(const DecodeArgs a) {
     }
 
     // ---- transpose-reduce over the RS row-group lanes (lane bits above LOG_CQ) ----
-    transpose_levels<NV / 2, LOG_CQ + LOG_NV - 1>(acc, lane);
-    const float red = sum_levels<LOG_CQ + LOG_RS - 1, LOG_CQ + LOG_NV>(acc[0]);
+    float red[NVL];
+    if constexpr (NVL == 1) {
+      transpose_levels<NV / 2, LOG_CQ + LOG_NV - 1>(acc, lane);
+      red[0] = sum_levels<LOG_CQ + LOG_RS - 1, LOG_CQ + LOG_NV>(acc[0]);
+    } else {
+      transpose_levels<NV / 2, LOG_CQ + LOG_RS - 1, LOG_RS>(acc, lane);
+#pragma unroll
+      for (int l = 0; l < NVL; ++l) red[l] = acc[l];
+    }
 
     // ---- u = v - a (to every lane of the column group); o = b + beta*(qh.kh)*u ----
-    if (holds_a && owner) u_tab[EPL * cq + m_final] = v_mine - red;
+    if (holds_a && owner) {
+#pragma unroll
+      for (int l = 0; l < NVL; ++l) u_tab[EPL * cq + m_final + l] = v_mine[l] - red[l];
+    }
     __syncthreads();
     float u[EPL];
 #pragma unroll
@@ -509,9 +541,16 @@ __global__ __launch_bounds__(kWave) void kda_decode_kfirst(const DecodeArgs a) {
       u[e + 2] = x.z;
       u[e + 3] = x.w;
     }
-    if (!holds_a && owner)
-      store_scalar<QBF16>(a.out, (static_cast<int64_t>(t) * a.HV + j.hv) * DV + my_col,
-                          fmaf(ts.beta * ts.qk, u[m_final & (EPL - 1)], red));
+    if (!holds_a && owner) {
+      const int64_t o_off = (static_cast<int64_t>(t) * a.HV + j.hv) * DV + my_col;
+      if constexpr (NVL == 1) {
+        store_scalar<QBF16>(a.out, o_off, fmaf(ts.beta * ts.qk, u[m_final & (EPL - 1)], red[0]));
+      } else {
+        const float o0 = fmaf(ts.beta * ts.qk, u[m_final & (EPL - 1)], red[0]);
+        const float o1 = fmaf(ts.beta * ts.qk, u[(m_final & (EPL - 1)) + 1], red[1]);
+        store_pair<QBF16>(a.out, o_off, o0, o1);
+      }
+    }
 
     // ---- S = alpha*S + (beta*kh) u^T ----
 #pragma unroll
@@ -724,17 +763,17 @@ constexpr size_t static_lds() {   // the kernels' tables: red_tab, upd_tab, u_ta
   return 2 * 2 * DK * sizeof(float2) + (DV < 32 ? DV : 32) * sizeof(float);
 }
 
-template <int DK, int DV, bool QBF16, bool SBF16, int LAYOUT, bool CONVV>
+template <int DK, int DV, bool QBF16, bool SBF16, int LAYOUT, bool CONVV, int CWT = 32>
 hipError_t launch_one(const DecodeArgs& args, hipStream_t stream) {
-  constexpr int CW = DV < 32 ? DV : 32;
+  constexpr int CW = DV < CWT ? DV : CWT;
   const int64_t nwg = static_cast<int64_t>(args.B) * args.HV * (DV / CW);
   void* kargs[] = {const_cast<DecodeArgs*>(&args)};
   const void* fn = LAYOUT == KDA_STATE_K_FIRST
-                       ? reinterpret_cast<const void*>(&kda_decode_kfirst<DK, DV, QBF16, SBF16, CONVV>)
+                       ? reinterpret_cast<const void*>(&kda_decode_kfirst<DK, DV, QBF16, SBF16, CONVV, CWT>)
                        : reinterpret_cast<const void*>(&kda_decode_vfirst<DK, DV, QBF16, SBF16, CONVV>);
   // workgroups per CU that hold about 128 KiB of state: 8 at d = 128, 16 at 64
   constexpr int kCapWgs = 32768 / (DK * CW);
-  static_assert(static_lds<DK, DV>() < capped_lds(kCapWgs), "cap above the tables");
+  static_assert(SBF16 || static_lds<DK, DV>() < capped_lds(kCapWgs), "cap above the tables");
   const bool cap = DK >= 64 && DV >= 64 && !SBF16 && args.T <= args.B &&
                    (LAYOUT == KDA_STATE_K_FIRST || nwg >= kCapMinWaves);
   // Multi-token batches at dk = dv = 64 on an fp32 pool keep six waves per
@@ -750,13 +789,32 @@ hipError_t launch_one(const DecodeArgs& args, hipStream_t stream) {
 
 using LaunchFn = hipError_t (*)(const DecodeArgs&, hipStream_t);
 
+// Key-first kernel on a bf16 pool: 64-column slabs make every slab row a
+// whole 128-byte line (32 bf16 columns are half a line, split between two
+// waves), at two waves per (request, head) tile and twice the registers per
+// lane (about 180: two waves per SIMD).  They win on large one-token
+// batches (96 heads x 256 requests: 339 -> 280 us) and lose where fewer,
+// heavier waves leave the chip short of work or the token loop is long
+// (32 heads x 64 requests +4%, 1..8 tokens +7%, 4 tokens +1%), so they are
+// taken for one-token batches of at least kCapMinWaves 32-column slabs.
+template <int DK, int DV, bool QBF16>
+hipError_t launch_kfirst_bf16(const DecodeArgs& args, hipStream_t stream) {
+  if constexpr (DV >= 64) {
+    const int64_t waves = static_cast<int64_t>(args.B) * args.HV * (DV / 32);
+    if (args.T <= args.B && waves >= kCapMinWaves)
+      return launch_one<DK, DV, QBF16, true, KDA_STATE_K_FIRST, false, 64>(args, stream);
+  }
+  return launch_one<DK, DV, QBF16, true, KDA_STATE_K_FIRST, false, 32>(args, stream);
+}
+
 template <int DK, int DV, bool QBF16, bool SBF16>
 LaunchFn pick_layout(int layout, bool conv_v) {
   if (layout == KDA_STATE_V_FIRST)
     return conv_v ? &launch_one<DK, DV, QBF16, SBF16, KDA_STATE_V_FIRST, true>
                   : &launch_one<DK, DV, QBF16, SBF16, KDA_STATE_V_FIRST, false>;
-  return conv_v ? &launch_one<DK, DV, QBF16, SBF16, KDA_STATE_K_FIRST, true>
-                : &launch_one<DK, DV, QBF16, SBF16, KDA_STATE_K_FIRST, false>;
+  if (conv_v) return &launch_one<DK, DV, QBF16, SBF16, KDA_STATE_K_FIRST, true>;
+  if constexpr (SBF16) return &launch_kfirst_bf16<DK, DV, QBF16>;
+  return &launch_one<DK, DV, QBF16, SBF16, KDA_STATE_K_FIRST, false>;
 }
 
 template <int DK, int DV>
