@@ -212,6 +212,67 @@ __device__ __forceinline__ void zero_rows(const DecodeArgs& a, const TileJob& j,
     if (lane < CW) store_scalar<BF16>(a.out, (static_cast<int64_t>(t) * a.HV + j.hv) * DV + j.slab * CW + lane, 0.0f);
 }
 
+// N (1 or 2) consecutive elements of one row, kept in storage form until
+// used, so that a load issued a token ahead is waited for only where its
+// value is taken.
+template <bool BF16, int N>
+struct RawRun {
+  static constexpr int W = (BF16 && N == 2) ? 1 : N;
+  uint32_t w[W];
+  __device__ __forceinline__ void load(const void* base, int64_t off) {
+    if constexpr (BF16 && N == 2) {
+      w[0] = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(base) + off);
+    } else if constexpr (BF16) {
+      w[0] = static_cast<const uint16_t*>(base)[off];
+    } else if constexpr (N == 2) {
+      const u32x2 x = *reinterpret_cast<const u32x2*>(static_cast<const float*>(base) + off);
+      w[0] = x[0];
+      w[1] = x[1];
+    } else {
+      w[0] = __float_as_uint(static_cast<const float*>(base)[off]);
+    }
+  }
+  __device__ __forceinline__ void unpack(float (&x)[N]) const {
+    if constexpr (BF16 && N == 2) {
+      x[0] = bf16_to_f32(w[0] & 0xffffu);
+      x[1] = __uint_as_float(w[0] & 0xffff0000u);
+    } else if constexpr (BF16) {
+      x[0] = bf16_to_f32(w[0]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < N; ++i) x[i] = __uint_as_float(w[i]);
+    }
+  }
+};
+
+// One token's inputs for one lane: q, k and the gate pre-activation of its
+// CPL setup channels (from channel c0s), the beta logit, and the NVL v
+// values at v_ch.  Every lane loads (a lane without channels reads channel
+// 0 and drops it), so the loads never sit in a divergent branch.
+template <int DK, int DV, bool QKBF16, bool VBF16, int CPL, int NVL>
+struct TokenInputs {
+  RawRun<QKBF16, CPL> q, k;
+  RawRun<false, CPL> x;
+  RawRun<VBF16, NVL> v;
+  float bl;
+  __device__ __forceinline__ void load(const DecodeArgs& a, const TileJob& j, int t, int c0s, int64_t v_ch) {
+    const int64_t qk_off = (static_cast<int64_t>(t) * a.H + j.h) * DK + c0s;
+    q.load(a.q, qk_off);
+    k.load(a.k, qk_off);
+    x.load(a.raw_gate, (static_cast<int64_t>(t) * a.HV + j.hv) * DK + c0s);
+    v.load(a.v, static_cast<int64_t>(t) * a.HV * DV + v_ch);
+    bl = a.beta_logits[static_cast<int64_t>(t) * a.HV + j.hv];
+  }
+};
+
+// Inputs one token ahead: measured in the same process against loading
+// each token's inputs (together) at its start, 1024 requests x 4 tokens x
+// 96 heads: bf16 pool value-first 1397 -> 1305 us, key-first 1444 -> 1449
+// us; fp32 pool 2270 -> 2285 us (key-first), 2259 -> 2300 us
+// (value-first), where the loop is bound by the state's HBM traffic.
+template <bool SBF16>
+constexpr bool kInputsAhead = SBF16;
+
 struct TokenScalars {
   float beta;   // write strength
   float qk;     // qh . kh, query scale included
@@ -220,21 +281,22 @@ struct TokenScalars {
 // Per-token setup, CPL channels per lane: L2 norms (wave reductions), gate,
 // beta; fills red_tab[c] = {kh*alpha, qh*alpha} and upd_tab[c] = {alpha,
 // beta*kh} for the wave's channels.
-template <int DK, int CPL, bool QBF16>
-__device__ __forceinline__ TokenScalars token_setup(const DecodeArgs& a, const TileJob& j, int t, int c0,
+template <int DK, int CPL, typename In>
+__device__ __forceinline__ TokenScalars token_setup(const DecodeArgs& a, const In& in, int c0,
                                                     bool chan_lane, const float (&dtb)[CPL], float amp,
                                                     float2* red_tab, float2* upd_tab) {
   float qv[CPL], kv[CPL], xg[CPL];
+  in.q.unpack(qv);
+  in.k.unpack(kv);
+  in.x.unpack(xg);
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) qv[c] = kv[c] = xg[c] = 0.0f;
-  if (chan_lane) {
-    const int64_t qk_off = (static_cast<int64_t>(t) * a.H + j.h) * DK + c0;
-    load_qk<QBF16, CPL>(a.q, qk_off, qv);
-    load_qk<QBF16, CPL>(a.k, qk_off, kv);
-    load_f32<CPL>(a.raw_gate + (static_cast<int64_t>(t) * a.HV + j.hv) * DK + c0, xg);
+  for (int c = 0; c < CPL; ++c) {
+    qv[c] = chan_lane ? qv[c] : 0.0f;
+    kv[c] = chan_lane ? kv[c] : 0.0f;
+    xg[c] = chan_lane ? xg[c] : 0.0f;
   }
   TokenScalars s;
-  s.beta = sigmoid_f(a.beta_logits[static_cast<int64_t>(t) * a.HV + j.hv]);
+  s.beta = sigmoid_f(in.bl);
   float sq = 0.0f, sk = 0.0f, sqk = 0.0f;
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
@@ -485,20 +547,32 @@ __global__ __launch_bounds__(kWave) void kda_decode_kfirst(const DecodeArgs a) {
   if constexpr (CONVV)
     if (holds_a) cv.load(a.conv_w_v, a.conv_win_v, j.slot, static_cast<int64_t>(a.HV) * DV, v_ch, a.conv_k, a.conv_w_bf16 != 0);
 
+  // A token's inputs are loaded together (every lane loads v, a column of
+  // its own slab), so their latencies overlap; with a bf16 pool, whose
+  // token loop is short of memory latency cover, one token ahead (see
+  // kInputsAhead).  With the convolution in front, q and k arrive convolved
+  // in fp32.
+  using In = TokenInputs<DK, DV, QBF16 && !CONVV, QBF16, CPL, NVL>;
+  constexpr bool kAhead = kInputsAhead<SBF16>;
+  const int c0s = chan_lane ? c0 : 0;
+  In nxt;
+  if constexpr (kAhead) nxt.load(a, j, j.t0, c0s, v_ch);
   int buf = 0;
   for (int t = j.t0; t < j.t1; ++t, buf ^= 1) {
-    float v_mine[NVL];
-    if constexpr (NVL == 1) {
-      v_mine[0] = holds_a ? load_scalar<QBF16>(a.v, static_cast<int64_t>(t) * a.HV * DV + v_ch) : 0.0f;
-      if constexpr (CONVV)
-        if (holds_a) v_mine[0] = cv.step(v_mine[0], a.conv_k);
+    In cur;
+    if constexpr (kAhead) {
+      cur = nxt;
+      if (t + 1 < j.t1) nxt.load(a, j, t + 1, c0s, v_ch);   // uniform
     } else {
-      v_mine[0] = v_mine[1] = 0.0f;
-      if (holds_a) load_qk<QBF16, 2>(a.v, static_cast<int64_t>(t) * a.HV * DV + v_ch, v_mine);
+      cur.load(a, j, t, c0s, v_ch);
     }
-    // with the convolution in front, q and k arrive convolved in fp32
-    const TokenScalars ts = token_setup<DK, CPL, QBF16 && !CONVV>(a, j, t, c0, chan_lane, dtb, amp,
-                                                                red_tab[buf], upd_tab[buf]);
+    float v_mine[NVL];
+    cur.v.unpack(v_mine);
+#pragma unroll
+    for (int l = 0; l < NVL; ++l) v_mine[l] = holds_a ? v_mine[l] : 0.0f;
+    if constexpr (CONVV)
+      if (holds_a) v_mine[0] = cv.step(v_mine[0], a.conv_k);
+    const TokenScalars ts = token_setup<DK, CPL>(a, cur, c0, chan_lane, dtb, amp, red_tab[buf], upd_tab[buf]);
     __syncthreads();
 
     // ---- one sweep: a = (kh*alpha)^T S, b = (qh*alpha)^T S, partial over rows ----
@@ -656,14 +730,28 @@ __global__ __launch_bounds__(kWave) void kda_decode_vfirst(const DecodeArgs a) {
   if constexpr (CONVV)
     if (holds_a) cv.load(a.conv_w_v, a.conv_win_v, j.slot, static_cast<int64_t>(a.HV) * DV, v_ch, a.conv_k, a.conv_w_bf16 != 0);
 
+  // the token's inputs loaded together, ahead with a bf16 pool (as in the
+  // key-first kernel)
+  using In = TokenInputs<DK, DV, QBF16 && !CONVV, QBF16, CPL, 1>;
+  constexpr bool kAhead = kInputsAhead<SBF16>;
+  const int c0s = chan_lane ? c0 : 0;
+  In nxt;
+  if constexpr (kAhead) nxt.load(a, j, j.t0, c0s, v_ch);
   int buf = 0;
   for (int t = j.t0; t < j.t1; ++t, buf ^= 1) {
-    float v_mine = holds_a ? load_scalar<QBF16>(a.v, static_cast<int64_t>(t) * a.HV * DV + v_ch) : 0.0f;
+    In cur;
+    if constexpr (kAhead) {
+      cur = nxt;
+      if (t + 1 < j.t1) nxt.load(a, j, t + 1, c0s, v_ch);   // uniform
+    } else {
+      cur.load(a, j, t, c0s, v_ch);
+    }
+    float vl[1];
+    cur.v.unpack(vl);
+    float v_mine = holds_a ? vl[0] : 0.0f;
     if constexpr (CONVV)
       if (holds_a) v_mine = cv.step(v_mine, a.conv_k);
-    // with the convolution in front, q and k arrive convolved in fp32
-    const TokenScalars ts = token_setup<DK, CPL, QBF16 && !CONVV>(a, j, t, c0, chan_lane, dtb, amp,
-                                                                red_tab[buf], upd_tab[buf]);
+    const TokenScalars ts = token_setup<DK, CPL>(a, cur, c0, chan_lane, dtb, amp, red_tab[buf], upd_tab[buf]);
     __syncthreads();
 
     // ---- sweep: per row, a and b partial over this lane's keys ----
