@@ -117,30 +117,6 @@ struct StateIO {
   }
 };
 
-// Channels [c0, c0 + CPL) of one token row of q / k (bf16 or f32).
-template <bool BF16, int CPL>
-__device__ __forceinline__ void load_qk(const void* base, int64_t off, float (&x)[CPL]) {
-  if constexpr (BF16) {
-    const uint16_t* p = static_cast<const uint16_t*>(base) + off;
-    if constexpr (CPL == 2) {
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
-      x[0] = bf16_to_f32(w & 0xffffu);
-      x[1] = __uint_as_float(w & 0xffff0000u);
-    } else {
-      x[0] = bf16_to_f32(p[0]);
-    }
-  } else {
-    const float* p = static_cast<const float*>(base) + off;
-    if constexpr (CPL == 2) {
-      const float2 w = *reinterpret_cast<const float2*>(p);
-      x[0] = w.x;
-      x[1] = w.y;
-    } else {
-      x[0] = p[0];
-    }
-  }
-}
-
 template <int CPL>
 __device__ __forceinline__ void load_f32(const float* p, float (&x)[CPL]) {
   if constexpr (CPL == 2) {
