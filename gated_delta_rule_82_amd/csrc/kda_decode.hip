@@ -856,16 +856,21 @@ using LaunchFn = hipError_t (*)(const DecodeArgs&, hipStream_t);
 // Key-first kernel on a bf16 pool: 64-column slabs make every slab row a
 // whole 128-byte line (32 bf16 columns are half a line, split between two
 // waves), at two waves per (request, head) tile and twice the registers per
-// lane (about 180: two waves per SIMD).  They win on large one-token
-// batches (96 heads x 256 requests: 339 -> 280 us) and lose where fewer,
-// heavier waves leave the chip short of work or the token loop is long
-// (32 heads x 64 requests +4%, 1..8 tokens +7%, 4 tokens +1%), so they are
-// taken for one-token batches of at least kCapMinWaves 32-column slabs.
+// lane (about 185: two waves per SIMD).  They win on large batches (96
+// heads x 256 requests, one token: 339 -> 280 us; 96 heads x 1024
+// requests: 2 tokens 1365 -> 1123 us, 4 tokens 1449 -> 1311 us; 96 heads x
+// 512 requests x 8 tokens 1110 -> 1017 us; 1..8 tokens over 96 heads x 128
+// requests 224 -> 199 us) and lose where fewer, heavier waves leave the
+// chip short of work: 32 heads x 64 requests, one token, +4%; 1..8 tokens
+// over 32 heads x 128 requests (16384 32-column slabs) +3.7%.  So they are
+// taken from kCapMinWaves 32-column slabs for one-token batches and from
+// twice that for longer ones (96 heads x 64 requests x 4 tokens, 24576
+// slabs, gains 3% with them and keeps 32 columns).
 template <int DK, int DV, bool QBF16>
 hipError_t launch_kfirst_bf16(const DecodeArgs& args, hipStream_t stream) {
   if constexpr (DV >= 64) {
     const int64_t waves = static_cast<int64_t>(args.B) * args.HV * (DV / 32);
-    if (args.T <= args.B && waves >= kCapMinWaves)
+    if (waves >= (args.T <= args.B ? kCapMinWaves : 2 * kCapMinWaves))
       return launch_one<DK, DV, QBF16, true, KDA_STATE_K_FIRST, false, 64>(args, stream);
   }
   return launch_one<DK, DV, QBF16, true, KDA_STATE_K_FIRST, false, 32>(args, stream);

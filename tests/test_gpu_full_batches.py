@@ -33,6 +33,7 @@ def torch_cuda():
     ("wide_b256_h96", "v_first", "f32"),
     ("wide_b256_h96", "k_first", "bf16"),
     ("stress_b1024_n4", "k_first", "f32"),
+    ("stress_b1024_n4", "k_first", "bf16"),   # 64-column slabs, 4 tokens
 ])
 def test_every_tile(torch_cuda, name, layout, sdt):
     torch = torch_cuda

@@ -98,18 +98,20 @@ def test_full_size_other_layouts(torch_cuda, name, sample, layout, sdt):
     torch_cuda.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("tokens,slabs", [("1", 16384), ("u:1..4", 32768)])
 @pytest.mark.parametrize("dk,dv", [(16, 64), (32, 64), (64, 64), (128, 64), (16, 128), (64, 128)])
-def test_kfirst_bf16_wide_slabs_every_tile(torch_cuda, dk, dv):
-    """One-token batches of at least 16384 32-column slabs on a key-first
-    bf16 pool run on 64-column slabs (two sums per lane after the
-    reduction); every tile of such a batch against the oracle, GQA, both
-    gate modes across the shapes, every other slot bit-identical."""
-    B = 16384 // (4 * dv // 32)
+def test_kfirst_bf16_wide_slabs_every_tile(torch_cuda, dk, dv, tokens, slabs):
+    """Batches of at least 16384 32-column slabs (one token per request) or
+    32768 (longer requests) on a key-first bf16 pool run on 64-column slabs
+    (two sums per lane after the reduction); every tile of such a batch
+    against the oracle, GQA, both gate modes across the shapes, every other
+    slot bit-identical."""
+    B = slabs // (4 * dv // 32)
     gate = wl.LOWER_BOUND if dk % 32 else wl.SOFTPLUS
-    cfg = wl.Workload(name="wide_slabs", B=B, H=2, HV=4, DK=dk, DV=dv, n_slots=B + 7, tokens="1",
+    cfg = wl.Workload(name="wide_slabs", B=B, H=2, HV=4, DK=dk, DV=dv, n_slots=B + 7, tokens=tokens,
                       gate_mode=gate, lower_bound=-5.0 if gate == wl.LOWER_BOUND else 0.0,
                       seed=31 + dk + dv, state_dtype="bf16")
-    _say("k-first bf16 wide slabs", dk, dv, B, gate)
+    _say("k-first bf16 wide slabs", dk, dv, B, tokens, gate)
     stats, _, _ = H.parity_case(wl.draw(cfg))
     print("wide slabs", dk, dv, stats, flush=True)
 
