@@ -252,15 +252,25 @@ constexpr bool kInputsAhead = SBF16;
 struct TokenScalars {
   float beta;   // write strength
   float qk;     // qh . kh, query scale included
+  bool fold;    // deferred decay: the pending factors are applied this token
 };
+
+// Deferred decay (key-first 64-column slabs).  The wave keeps its slab as
+// S = D o S^ with D the pending decay of each key row, so a token's write is
+// one FMA per element, S^ += (beta kh / D') u^T, instead of a multiply and
+// an FMA; the reads take kh o D' and qh o D'.  D' = D alpha is folded into
+// S^ (and reset to 1) on a request's last token and whenever some row's D'
+// would drop below kDeferFloor, which keeps every 1 / D' finite.
+constexpr float kDeferFloor = 5.421010862427522e-20f;   // 2^-64
 
 // Per-token setup, CPL channels per lane: L2 norms (wave reductions), gate,
 // beta; fills red_tab[c] = {kh*alpha, qh*alpha} and upd_tab[c] = {alpha,
 // beta*kh} for the wave's channels.
-template <int DK, int CPL, typename In>
+template <int DK, int CPL, typename In, bool DEFER = false>
 __device__ __forceinline__ TokenScalars token_setup(const DecodeArgs& a, const In& in, int c0,
                                                     bool chan_lane, const float (&dtb)[CPL], float amp,
-                                                    float2* red_tab, float2* upd_tab) {
+                                                    float2* red_tab, float2* upd_tab,
+                                                    float (&pend)[CPL], bool last) {
   float qv[CPL], kv[CPL], xg[CPL];
   in.q.unpack(qv);
   in.k.unpack(kv);
@@ -286,18 +296,40 @@ __device__ __forceinline__ TokenScalars token_setup(const DecodeArgs& a, const I
   const float rq = a.scale * rsqrt_f(sq + a.l2_eps);
   const float rk = rsqrt_f(sk + a.l2_eps);
   s.qk = sqk * rq * rk;
+  float alpha[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const float x = xg[c] + dtb[c];
+    const float g = a.gate_mode == KDA_GATE_SOFTPLUS ? -amp * softplus_f(x)
+                                                     : a.lower_bound * sigmoid_f(amp * x);
+    alpha[c] = exp_f(g);
+  }
+  s.fold = true;
+  if constexpr (DEFER) {
+    bool small = false;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      alpha[c] *= pend[c];                 // D' = D alpha
+      small |= chan_lane && !(alpha[c] >= kDeferFloor);
+    }
+    s.fold = last || __any(small);
+  }
   if (chan_lane) {
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-      const float x = xg[c] + dtb[c];
-      const float g = a.gate_mode == KDA_GATE_SOFTPLUS ? -amp * softplus_f(x)
-                                                       : a.lower_bound * sigmoid_f(amp * x);
-      const float alpha = exp_f(g);
       const float kh = kv[c] * rk;
       const float qh = qv[c] * rq;
-      red_tab[c0 + c] = make_float2(kh * alpha, qh * alpha);
-      upd_tab[c0 + c] = make_float2(alpha, s.beta * kh);
+      // reads take the decay unless it is applied to the slab this token;
+      // a deferred write is scaled by 1 / D'
+      const float m = (DEFER && s.fold) ? 1.0f : alpha[c];
+      const float w = (DEFER && !s.fold) ? __builtin_amdgcn_rcpf(alpha[c]) : 1.0f;
+      red_tab[c0 + c] = make_float2(kh * m, qh * m);
+      upd_tab[c0 + c] = make_float2(alpha[c], s.beta * kh * w);
     }
+  }
+  if constexpr (DEFER) {
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) pend[c] = s.fold ? 1.0f : alpha[c];
   }
   return s;
 }
@@ -530,6 +562,10 @@ __global__ __launch_bounds__(kWave) void kda_decode_kfirst(const DecodeArgs a) {
   // in fp32.
   using In = TokenInputs<DK, DV, QBF16 && !CONVV, QBF16, CPL, NVL>;
   constexpr bool kAhead = kInputsAhead<SBF16>;
+  constexpr bool kDefer = CWT == 64;
+  float pend[CPL];   // deferred decay of the lane's setup channels
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) pend[c] = 1.0f;
   const int c0s = chan_lane ? c0 : 0;
   In nxt;
   if constexpr (kAhead) nxt.load(a, j, j.t0, c0s, v_ch);
@@ -548,8 +584,19 @@ __global__ __launch_bounds__(kWave) void kda_decode_kfirst(const DecodeArgs a) {
     for (int l = 0; l < NVL; ++l) v_mine[l] = holds_a ? v_mine[l] : 0.0f;
     if constexpr (CONVV)
       if (holds_a) v_mine[0] = cv.step(v_mine[0], a.conv_k);
-    const TokenScalars ts = token_setup<DK, CPL>(a, cur, c0, chan_lane, dtb, amp, red_tab[buf], upd_tab[buf]);
+    const TokenScalars ts = token_setup<DK, CPL, In, kDefer>(a, cur, c0, chan_lane, dtb, amp, red_tab[buf],
+                                                           upd_tab[buf], pend, t + 1 == j.t1);
     __syncthreads();
+    if constexpr (kDefer) {
+      if (ts.fold) {   // uniform: apply the pending decay, this token's included
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+          const float f = upd_tab[buf][rs + RS * i].x;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) S[i][e] *= f;
+        }
+      }
+    }
 
     // ---- one sweep: a = (kh*alpha)^T S, b = (qh*alpha)^T S, partial over rows ----
     float acc[NV];
@@ -602,12 +649,12 @@ __global__ __launch_bounds__(kWave) void kda_decode_kfirst(const DecodeArgs a) {
       }
     }
 
-    // ---- S = alpha*S + (beta*kh) u^T ----
+    // ---- S = alpha*S + (beta*kh) u^T, or S^ += (beta*kh / D') u^T ----
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       const float2 p = upd_tab[buf][rs + RS * i];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) S[i][e] = fmaf(p.y, u[e], p.x * S[i][e]);
+      for (int e = 0; e < EPL; ++e) S[i][e] = fmaf(p.y, u[e], kDefer ? S[i][e] : p.x * S[i][e]);
     }
   }
 
@@ -727,7 +774,9 @@ __global__ __launch_bounds__(kWave) void kda_decode_vfirst(const DecodeArgs a) {
     float v_mine = holds_a ? vl[0] : 0.0f;
     if constexpr (CONVV)
       if (holds_a) v_mine = cv.step(v_mine, a.conv_k);
-    const TokenScalars ts = token_setup<DK, CPL>(a, cur, c0, chan_lane, dtb, amp, red_tab[buf], upd_tab[buf]);
+    float pend_unused[CPL];
+    const TokenScalars ts = token_setup<DK, CPL>(a, cur, c0, chan_lane, dtb, amp, red_tab[buf], upd_tab[buf],
+                                                 pend_unused, true);
     __syncthreads();
 
     // ---- sweep: per row, a and b partial over this lane's keys ----

@@ -78,6 +78,25 @@ def test_decode_degenerate_inputs(torch_cuda, gate, qkv, layout, sdt, DK, DV):
     print(stats, flush=True)
 
 
+@pytest.mark.parametrize("gate", [wl.SOFTPLUS, wl.LOWER_BOUND])
+def test_decode_degenerate_inputs_wide_bf16_slabs(torch_cuda, gate):
+    """The degenerate tokens on a batch large enough for the key-first bf16
+    pool's 64-column slabs with deferred decay (32768 32-column slabs, 9 to
+    12 tokens per request): decays to exactly zero and underflowing ones
+    force the pending factors to be folded in mid-request; sampled tiles
+    against the oracle."""
+    B = 2048
+    counts = 9 + np.arange(B) % 4
+    cu = tuple(int(x) for x in np.concatenate([[0], np.cumsum(counts)]))
+    cfg = wl.Workload(name="degenerate_wide", B=B, H=2, HV=4, DK=128, DV=128, n_slots=B + 5,
+                      cu_seqlens=cu, qkv_dtype="bf16", gate_mode=gate,
+                      lower_bound=-5.0 if gate == wl.LOWER_BOUND else 0.0, seed=13,
+                      state_layout="k_first", state_dtype="bf16")
+    _say("decode degenerate, 64-column bf16 slabs", gate, B)
+    stats, _, _ = H.parity_case(plant(wl.draw(cfg)), sample=96)
+    print("degenerate wide slabs", gate, stats, flush=True)
+
+
 @pytest.mark.parametrize("matmul", ["split_bf16", "f32"])
 @pytest.mark.parametrize("gate", [wl.SOFTPLUS, wl.LOWER_BOUND])
 @pytest.mark.parametrize("layout", ["v_first", "k_first"])
