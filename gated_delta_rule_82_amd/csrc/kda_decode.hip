@@ -394,6 +394,85 @@ struct ConvChannel {
   }
 };
 
+// The same for N adjacent channels (N = 1 or 2; the first one even), each
+// window, tap, input and output row read or written as one N-element
+// access: with two channels per lane a wave's access is 512 contiguous
+// bytes instead of two 4-byte strided ones.
+template <int N>
+struct ConvChannels {
+  float win[kMaxConvK - 1][N];
+  float tap[kMaxConvK][N];
+
+  template <bool BF16>
+  static __device__ __forceinline__ void load_run(const void* base, int64_t off, float (&x)[N]) {
+    if constexpr (N == 2) {
+      if constexpr (BF16) {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(base) + off);
+        x[0] = bf16_to_f32(w & 0xffffu);
+        x[1] = __uint_as_float(w & 0xffff0000u);
+      } else {
+        const float2 w = *reinterpret_cast<const float2*>(static_cast<const float*>(base) + off);
+        x[0] = w.x;
+        x[1] = w.y;
+      }
+    } else {
+      x[0] = load_scalar<BF16>(base, off);
+    }
+  }
+  static __device__ __forceinline__ void store_run(float* base, int64_t off, const float (&x)[N]) {
+    if constexpr (N == 2) *reinterpret_cast<float2*>(base + off) = make_float2(x[0], x[1]);
+    else base[off] = x[0];
+  }
+
+  __device__ __forceinline__ void load(const void* w, const float* window, int64_t slot, int64_t C,
+                                       int64_t ch, int K, bool w_bf16) {
+#pragma unroll
+    for (int q = 0; q < kMaxConvK; ++q) {
+      if (q < K) {
+        if (w_bf16) load_run<true>(w, q * C + ch, tap[q]);
+        else load_run<false>(w, q * C + ch, tap[q]);
+      } else {
+#pragma unroll
+        for (int c = 0; c < N; ++c) tap[q][c] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kMaxConvK - 1; ++q) {
+      if (q < K - 1) {
+        load_run<false>(window, (slot * (K - 1) + q) * C + ch, win[q]);
+      } else {
+#pragma unroll
+        for (int c = 0; c < N; ++c) win[q][c] = 0.0f;
+      }
+    }
+  }
+
+  // as ConvChannel::step, per channel
+  __device__ __forceinline__ void step(const float (&x)[N], int K, float (&y)[N]) {
+#pragma unroll
+    for (int c = 0; c < N; ++c) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int q = 0; q < kMaxConvK; ++q) {
+        const float in = q < K - 1 ? win[q < kMaxConvK - 1 ? q : 0][c] : x[c];
+        if (q < K) acc = fmaf(tap[q][c], in, acc);
+      }
+#pragma unroll
+      for (int q = 0; q < kMaxConvK - 1; ++q) {
+        const float next = q + 1 < kMaxConvK - 1 ? win[q + 1 < kMaxConvK - 1 ? q + 1 : 0][c] : x[c];
+        win[q][c] = q < K - 2 ? next : (q == K - 2 ? x[c] : win[q][c]);
+      }
+      y[c] = silu_f(acc);
+    }
+  }
+
+  __device__ __forceinline__ void store(float* window, int64_t slot, int64_t C, int64_t ch, int K) const {
+#pragma unroll
+    for (int q = 0; q < kMaxConvK - 1; ++q)
+      if (q < K - 1) store_run(window, (slot * (K - 1) + q) * C + ch, win[q]);
+  }
+};
+
 // q and k of every (request, key head): one workgroup per (request, key
 // head, stream), CPL channels per lane, fp32 results.  A lane reads and
 // writes only its own channels' windows, so the in-place window update needs
@@ -422,18 +501,16 @@ __global__ __launch_bounds__(kWave) void kda_conv_qk(const ConvQKArgs a) {
     return;
   }
   if (t0 == t1) return;
-  ConvChannel cv[CPL];
-#pragma unroll
-  for (int c = 0; c < CPL; ++c) cv[c].load(a.w[s], a.win[s], slot, C, ch + c, a.conv_k, a.w_bf16 != 0);
+  ConvChannels<CPL> cv;
+  cv.load(a.w[s], a.win[s], slot, C, ch, a.conv_k, a.w_bf16 != 0);
   for (int t = t0; t < t1; ++t) {
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      const int64_t off = static_cast<int64_t>(t) * C + ch + c;
-      store_scalar<false>(a.y[s], off, cv[c].step(load_scalar<XBF16>(a.x[s], off), a.conv_k));
-    }
+    const int64_t off = static_cast<int64_t>(t) * C + ch;
+    float x[CPL], y[CPL];
+    ConvChannels<CPL>::template load_run<XBF16>(a.x[s], off, x);
+    cv.step(x, a.conv_k, y);
+    ConvChannels<CPL>::store_run(static_cast<float*>(a.y[s]), off, y);
   }
-#pragma unroll
-  for (int c = 0; c < CPL; ++c) cv[c].store(a.win[s], slot, C, ch + c, a.conv_k);
+  cv.store(a.win[s], slot, C, ch, a.conv_k);
 }
 
 // ---------------------------------------------------------------------------
