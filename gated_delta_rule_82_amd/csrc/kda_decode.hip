@@ -675,7 +675,8 @@ __global__ __launch_bounds__(kWave) void kda_decode_kfirst(const DecodeArgs a) {
       }
     }
 
-    // ---- one sweep: a = (kh*alpha)^T S, b = (qh*alpha)^T S, partial over rows ----
+    // ---- one sweep: a = (kh*alpha)^T S, b = (qh*alpha)^T S (deferred: against
+    // kh*D', qh*D' and S^), partial over rows ----
     float acc[NV];
 #pragma unroll
     for (int m = 0; m < NV; ++m) acc[m] = 0.0f;
