@@ -255,12 +255,17 @@ struct TokenScalars {
   bool fold;    // deferred decay: the pending factors are applied this token
 };
 
-// Deferred decay (key-first 64-column slabs).  The wave keeps its slab as
-// S = D o S^ with D the pending decay of each key row, so a token's write is
-// one FMA per element, S^ += (beta kh / D') u^T, instead of a multiply and
-// an FMA; the reads take kh o D' and qh o D'.  D' = D alpha is folded into
-// S^ (and reset to 1) on a request's last token and whenever some row's D'
-// would drop below kDeferFloor, which keeps every 1 / D' finite.
+// Deferred decay (key-first 64-column slabs; value-first slabs on a bf16
+// pool).  The wave keeps its slab as S = D o S^ with D the pending decay of
+// each key, so a token's write is one FMA per element, S^ += (beta kh / D')
+// u^T, instead of a multiply and an FMA; the reads take kh o D' and
+// qh o D'.  D' = D alpha is folded into S^ (and reset to 1) on a request's
+// last token and whenever some key's D' would drop below kDeferFloor,
+// which keeps every 1 / D' finite.  Measured where the token loop is short
+// of issue slots: two waves per SIMD (key-first 64-column slabs, 96 heads x
+// 1024 requests x 4 tokens 1323 -> 1279 us) or a bf16 pool (value-first,
+// same batch 1353 -> 1323 us; 8 tokens -4%, 1..8 tokens -4%); with four
+// waves per SIMD on 32-column key-first slabs it gained at most 2%.
 constexpr float kDeferFloor = 5.421010862427522e-20f;   // 2^-64
 
 // Per-token setup, CPL channels per lane: L2 norms (wave reductions), gate,
@@ -835,6 +840,10 @@ __global__ __launch_bounds__(kWave) void kda_decode_vfirst(const DecodeArgs a) {
   // key-first kernel)
   using In = TokenInputs<DK, DV, QBF16 && !CONVV, QBF16, CPL, 1>;
   constexpr bool kAhead = kInputsAhead<SBF16>;
+  constexpr bool kDefer = SBF16;   // see kDeferFloor
+  float pend[CPL];   // deferred decay of the lane's setup channels
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) pend[c] = 1.0f;
   const int c0s = chan_lane ? c0 : 0;
   In nxt;
   if constexpr (kAhead) nxt.load(a, j, j.t0, c0s, v_ch);
@@ -852,10 +861,27 @@ __global__ __launch_bounds__(kWave) void kda_decode_vfirst(const DecodeArgs a) {
     float v_mine = holds_a ? vl[0] : 0.0f;
     if constexpr (CONVV)
       if (holds_a) v_mine = cv.step(v_mine, a.conv_k);
-    float pend_unused[CPL];
-    const TokenScalars ts = token_setup<DK, CPL>(a, cur, c0, chan_lane, dtb, amp, red_tab[buf], upd_tab[buf],
-                                                 pend_unused, true);
+    const TokenScalars ts = token_setup<DK, CPL, In, kDefer>(a, cur, c0, chan_lane, dtb, amp, red_tab[buf],
+                                                           upd_tab[buf], pend, t + 1 == j.t1);
     __syncthreads();
+    if constexpr (kDefer) {
+      if (ts.fold) {   // uniform: apply the pending decay (per key), this token's included
+        float f[EPL];
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+          const float4 p01 = *reinterpret_cast<const float4*>(&upd_tab[buf][key0 + QSTRIDE * q]);
+          const float4 p23 = *reinterpret_cast<const float4*>(&upd_tab[buf][key0 + QSTRIDE * q + 2]);
+          f[4 * q] = p01.x;
+          f[4 * q + 1] = p01.z;
+          f[4 * q + 2] = p23.x;
+          f[4 * q + 3] = p23.z;
+        }
+#pragma unroll
+        for (int i = 0; i < L; ++i)
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) S[i][e] *= f[e];
+      }
+    }
 
     // ---- sweep: per row, a and b partial over this lane's keys ----
     float kq[EPL], qq[EPL];   // kh*alpha, qh*alpha of the lane's keys
@@ -907,7 +933,7 @@ __global__ __launch_bounds__(kWave) void kda_decode_vfirst(const DecodeArgs a) {
     for (int i = 0; i < L; ++i) {
       const float u = u_tab[rsub * L + i];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) S[i][e] = fmaf(bk[e], u, al[e] * S[i][e]);
+      for (int e = 0; e < EPL; ++e) S[i][e] = fmaf(bk[e], u, kDefer ? S[i][e] : al[e] * S[i][e]);
     }
   }
 

@@ -69,6 +69,7 @@ def work(gate, qkv, layout, sdt, DK=32, DV=32, seed=11):
     ("bf16", "v_first", "f32", 128, 128),
     ("bf16", "k_first", "f32", 128, 128),
     ("bf16", "k_first", "bf16", 64, 32),
+    ("bf16", "v_first", "bf16", 128, 128),   # deferred decay on a bf16 pool
 ])
 def test_decode_degenerate_inputs(torch_cuda, gate, qkv, layout, sdt, DK, DV):
     cfg = work(gate, qkv, layout, sdt, DK, DV)
