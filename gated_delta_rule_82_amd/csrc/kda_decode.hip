@@ -255,17 +255,18 @@ struct TokenScalars {
   bool fold;    // deferred decay: the pending factors are applied this token
 };
 
-// Deferred decay (key-first 64-column slabs; value-first slabs on a bf16
-// pool).  The wave keeps its slab as S = D o S^ with D the pending decay of
-// each key, so a token's write is one FMA per element, S^ += (beta kh / D')
-// u^T, instead of a multiply and an FMA; the reads take kh o D' and
-// qh o D'.  D' = D alpha is folded into S^ (and reset to 1) on a request's
-// last token and whenever some key's D' would drop below kDeferFloor,
-// which keeps every 1 / D' finite.  Measured where the token loop is short
-// of issue slots: two waves per SIMD (key-first 64-column slabs, 96 heads x
-// 1024 requests x 4 tokens 1323 -> 1279 us) or a bf16 pool (value-first,
-// same batch 1353 -> 1323 us; 8 tokens -4%, 1..8 tokens -4%); with four
-// waves per SIMD on 32-column key-first slabs it gained at most 2%.
+// Deferred decay (both kernels on a bf16 pool).  The wave keeps its slab
+// as S = D o S^ with D the pending decay of each key, so a token's write is
+// one FMA per element, S^ += (beta kh / D') u^T, instead of a multiply and
+// an FMA; the reads take kh o D' and qh o D'.  D' = D alpha is folded into
+// S^ (and reset to 1) on a request's last token and whenever some key's D'
+// would drop below kDeferFloor, which keeps every 1 / D' finite.  Measured
+// in the same process on bf16 pools, where the multi-token loop is short of
+// issue slots: key-first 64-column slabs, 96 heads x 1024 requests x 4
+// tokens 1323 -> 1279 us; 32-column slabs, 1..8 tokens over 32 heads x 128
+// requests 77.0 -> 72.7 us; value-first, 4 tokens 1353 -> 1323 us, 1..8
+// tokens 79.9 -> 76.6 us; one-token batches within 1%.  On an fp32 pool the
+// loop is bound by the state's HBM traffic (no gain measured).
 constexpr float kDeferFloor = 5.421010862427522e-20f;   // 2^-64
 
 // Per-token setup, CPL channels per lane: L2 norms (wave reductions), gate,
@@ -644,7 +645,7 @@ __global__ __launch_bounds__(kWave) void kda_decode_kfirst(const DecodeArgs a) {
   // in fp32.
   using In = TokenInputs<DK, DV, QBF16 && !CONVV, QBF16, CPL, NVL>;
   constexpr bool kAhead = kInputsAhead<SBF16>;
-  constexpr bool kDefer = CWT == 64;
+  constexpr bool kDefer = SBF16;   // see kDeferFloor
   float pend[CPL];   // deferred decay of the lane's setup channels
 #pragma unroll
   for (int c = 0; c < CPL; ++c) pend[c] = 1.0f;
