@@ -255,24 +255,26 @@ struct TokenScalars {
   bool fold;    // deferred decay: the pending factors are applied this token
 };
 
-// Deferred decay (both kernels on a bf16 pool).  The wave keeps its slab
-// as S = D o S^ with D the pending decay of each key, so a token's write is
-// one FMA per element, S^ += (beta kh / D') u^T, instead of a multiply and
-// an FMA; the reads take kh o D' and qh o D'.  D' = D alpha is folded into
-// S^ (and reset to 1) on a request's last token and whenever some key's D'
-// would drop below kDeferFloor, which keeps every 1 / D' finite.  Measured
-// in the same process on bf16 pools, where the multi-token loop is short of
-// issue slots: key-first 64-column slabs, 96 heads x 1024 requests x 4
-// tokens 1323 -> 1279 us; 32-column slabs, 1..8 tokens over 32 heads x 128
-// requests 77.0 -> 72.7 us; value-first, 4 tokens 1353 -> 1323 us, 1..8
-// tokens 79.9 -> 76.6 us; one-token batches within 1%.  On an fp32 pool the
-// loop is bound by the state's HBM traffic (no gain measured).
+// Deferred decay.  The wave keeps its slab as S = D o S^ with D the pending
+// decay of each key, so a token's write is one FMA per element,
+// S^ += (beta kh / D') u^T, instead of a multiply and an FMA; the reads take
+// kh o D' and qh o D'.  D' = D alpha is folded into S^ (and reset to 1) on a
+// request's last token and whenever some key's D' would drop below
+// kDeferFloor, which keeps every 1 / D' finite.  Measured in the same
+// process against the plain update: key-first 64-column bf16 slabs, 96
+// heads x 1024 requests x 4 tokens 1323 -> 1279 us; 32-column bf16 slabs,
+// 1..8 tokens over 32 heads x 128 requests 77.0 -> 72.7 us; value-first
+// bf16, 4 tokens 1353 -> 1323 us, 1..8 tokens 79.9 -> 76.6 us; fp32 pools,
+// 1..8 tokens 113.0 -> 110.1 us (key-first) and 109.8 -> 109.2 us
+// (value-first), the rest within 0.4%.
 constexpr float kDeferFloor = 5.421010862427522e-20f;   // 2^-64
 
 // Per-token setup, CPL channels per lane: L2 norms (wave reductions), gate,
-// beta; fills red_tab[c] = {kh*alpha, qh*alpha} and upd_tab[c] = {alpha,
-// beta*kh} for the wave's channels.
-template <int DK, int CPL, typename In, bool DEFER = false>
+// beta, the deferred decay D' = D alpha (pend holds D across tokens); fills
+// red_tab[c] = {kh*D', qh*D'} and upd_tab[c] = {D', beta*kh/D'} for the
+// wave's channels, or, on a folding token, {kh, qh} and {D', beta*kh} (the
+// kernel then scales its slab's key rows by D').
+template <int DK, int CPL, typename In>
 __device__ __forceinline__ TokenScalars token_setup(const DecodeArgs& a, const In& in, int c0,
                                                     bool chan_lane, const float (&dtb)[CPL], float amp,
                                                     float2* red_tab, float2* upd_tab,
@@ -310,16 +312,13 @@ __device__ __forceinline__ TokenScalars token_setup(const DecodeArgs& a, const I
                                                      : a.lower_bound * sigmoid_f(amp * x);
     alpha[c] = exp_f(g);
   }
-  s.fold = true;
-  if constexpr (DEFER) {
-    bool small = false;
+  bool small = false;
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      alpha[c] *= pend[c];                 // D' = D alpha
-      small |= chan_lane && !(alpha[c] >= kDeferFloor);
-    }
-    s.fold = last || __any(small);
+  for (int c = 0; c < CPL; ++c) {
+    alpha[c] *= pend[c];                 // D' = D alpha
+    small |= chan_lane && !(alpha[c] >= kDeferFloor);
   }
+  s.fold = last || __any(small);
   if (chan_lane) {
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
@@ -327,16 +326,14 @@ __device__ __forceinline__ TokenScalars token_setup(const DecodeArgs& a, const I
       const float qh = qv[c] * rq;
       // reads take the decay unless it is applied to the slab this token;
       // a deferred write is scaled by 1 / D'
-      const float m = (DEFER && s.fold) ? 1.0f : alpha[c];
-      const float w = (DEFER && !s.fold) ? __builtin_amdgcn_rcpf(alpha[c]) : 1.0f;
+      const float m = s.fold ? 1.0f : alpha[c];
+      const float w = s.fold ? 1.0f : __builtin_amdgcn_rcpf(alpha[c]);
       red_tab[c0 + c] = make_float2(kh * m, qh * m);
       upd_tab[c0 + c] = make_float2(alpha[c], s.beta * kh * w);
     }
   }
-  if constexpr (DEFER) {
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) pend[c] = s.fold ? 1.0f : alpha[c];
-  }
+  for (int c = 0; c < CPL; ++c) pend[c] = s.fold ? 1.0f : alpha[c];
   return s;
 }
 
@@ -645,7 +642,6 @@ __global__ __launch_bounds__(kWave) void kda_decode_kfirst(const DecodeArgs a) {
   // in fp32.
   using In = TokenInputs<DK, DV, QBF16 && !CONVV, QBF16, CPL, NVL>;
   constexpr bool kAhead = kInputsAhead<SBF16>;
-  constexpr bool kDefer = SBF16;   // see kDeferFloor
   float pend[CPL];   // deferred decay of the lane's setup channels
 #pragma unroll
   for (int c = 0; c < CPL; ++c) pend[c] = 1.0f;
@@ -667,17 +663,15 @@ __global__ __launch_bounds__(kWave) void kda_decode_kfirst(const DecodeArgs a) {
     for (int l = 0; l < NVL; ++l) v_mine[l] = holds_a ? v_mine[l] : 0.0f;
     if constexpr (CONVV)
       if (holds_a) v_mine[0] = cv.step(v_mine[0], a.conv_k);
-    const TokenScalars ts = token_setup<DK, CPL, In, kDefer>(a, cur, c0, chan_lane, dtb, amp, red_tab[buf],
-                                                           upd_tab[buf], pend, t + 1 == j.t1);
+    const TokenScalars ts = token_setup<DK, CPL>(a, cur, c0, chan_lane, dtb, amp, red_tab[buf], upd_tab[buf],
+                                                 pend, t + 1 == j.t1);
     __syncthreads();
-    if constexpr (kDefer) {
-      if (ts.fold) {   // uniform: apply the pending decay, this token's included
+    if (ts.fold) {   // uniform: apply the pending decay, this token's included
 #pragma unroll
-        for (int i = 0; i < R; ++i) {
-          const float f = upd_tab[buf][rs + RS * i].x;
+      for (int i = 0; i < R; ++i) {
+        const float f = upd_tab[buf][rs + RS * i].x;
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) S[i][e] *= f;
-        }
+        for (int e = 0; e < EPL; ++e) S[i][e] *= f;
       }
     }
 
@@ -733,12 +727,12 @@ __global__ __launch_bounds__(kWave) void kda_decode_kfirst(const DecodeArgs a) {
       }
     }
 
-    // ---- S = alpha*S + (beta*kh) u^T, or S^ += (beta*kh / D') u^T ----
+    // ---- S^ += (beta*kh / D') u^T (the decay is in D' or already applied) ----
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-      const float2 p = upd_tab[buf][rs + RS * i];
+      const float py = upd_tab[buf][rs + RS * i].y;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) S[i][e] = fmaf(p.y, u[e], kDefer ? S[i][e] : p.x * S[i][e]);
+      for (int e = 0; e < EPL; ++e) S[i][e] = fmaf(py, u[e], S[i][e]);
     }
   }
 
@@ -841,7 +835,6 @@ __global__ __launch_bounds__(kWave) void kda_decode_vfirst(const DecodeArgs a) {
   // key-first kernel)
   using In = TokenInputs<DK, DV, QBF16 && !CONVV, QBF16, CPL, 1>;
   constexpr bool kAhead = kInputsAhead<SBF16>;
-  constexpr bool kDefer = SBF16;   // see kDeferFloor
   float pend[CPL];   // deferred decay of the lane's setup channels
 #pragma unroll
   for (int c = 0; c < CPL; ++c) pend[c] = 1.0f;
@@ -862,26 +855,24 @@ __global__ __launch_bounds__(kWave) void kda_decode_vfirst(const DecodeArgs a) {
     float v_mine = holds_a ? vl[0] : 0.0f;
     if constexpr (CONVV)
       if (holds_a) v_mine = cv.step(v_mine, a.conv_k);
-    const TokenScalars ts = token_setup<DK, CPL, In, kDefer>(a, cur, c0, chan_lane, dtb, amp, red_tab[buf],
-                                                           upd_tab[buf], pend, t + 1 == j.t1);
+    const TokenScalars ts = token_setup<DK, CPL>(a, cur, c0, chan_lane, dtb, amp, red_tab[buf], upd_tab[buf],
+                                                 pend, t + 1 == j.t1);
     __syncthreads();
-    if constexpr (kDefer) {
-      if (ts.fold) {   // uniform: apply the pending decay (per key), this token's included
-        float f[EPL];
+    if (ts.fold) {   // uniform: apply the pending decay (per key), this token's included
+      float f[EPL];
 #pragma unroll
-        for (int q = 0; q < Q; ++q) {
-          const float4 p01 = *reinterpret_cast<const float4*>(&upd_tab[buf][key0 + QSTRIDE * q]);
-          const float4 p23 = *reinterpret_cast<const float4*>(&upd_tab[buf][key0 + QSTRIDE * q + 2]);
-          f[4 * q] = p01.x;
-          f[4 * q + 1] = p01.z;
-          f[4 * q + 2] = p23.x;
-          f[4 * q + 3] = p23.z;
-        }
-#pragma unroll
-        for (int i = 0; i < L; ++i)
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) S[i][e] *= f[e];
+      for (int q = 0; q < Q; ++q) {
+        const float4 p01 = *reinterpret_cast<const float4*>(&upd_tab[buf][key0 + QSTRIDE * q]);
+        const float4 p23 = *reinterpret_cast<const float4*>(&upd_tab[buf][key0 + QSTRIDE * q + 2]);
+        f[4 * q] = p01.x;
+        f[4 * q + 1] = p01.z;
+        f[4 * q + 2] = p23.x;
+        f[4 * q + 3] = p23.z;
       }
+#pragma unroll
+      for (int i = 0; i < L; ++i)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) S[i][e] *= f[e];
     }
 
     // ---- sweep: per row, a and b partial over this lane's keys ----
@@ -919,22 +910,22 @@ __global__ __launch_bounds__(kWave) void kda_decode_vfirst(const DecodeArgs a) {
       store_scalar<QBF16>(a.out, (static_cast<int64_t>(t) * a.HV + j.hv) * DV + my_row,
                           fmaf(ts.beta * ts.qk, u_tab[rsub * L + i_final], red));
 
-    // ---- S = alpha*S + (beta*kh) u^T ----
-    float al[EPL], bk[EPL];   // alpha, beta*kh of the lane's keys
+    // ---- S^ += (beta*kh / D') u^T (the decay is in D' or already applied) ----
+    float bk[EPL];   // beta*kh / D' of the lane's keys
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
       const float4 p01 = *reinterpret_cast<const float4*>(&upd_tab[buf][key0 + QSTRIDE * q]);
       const float4 p23 = *reinterpret_cast<const float4*>(&upd_tab[buf][key0 + QSTRIDE * q + 2]);
-      al[4 * q] = p01.x;  bk[4 * q] = p01.y;
-      al[4 * q + 1] = p01.z;  bk[4 * q + 1] = p01.w;
-      al[4 * q + 2] = p23.x;  bk[4 * q + 2] = p23.y;
-      al[4 * q + 3] = p23.z;  bk[4 * q + 3] = p23.w;
+      bk[4 * q] = p01.y;
+      bk[4 * q + 1] = p01.w;
+      bk[4 * q + 2] = p23.y;
+      bk[4 * q + 3] = p23.w;
     }
 #pragma unroll
     for (int i = 0; i < L; ++i) {
       const float u = u_tab[rsub * L + i];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) S[i][e] = fmaf(bk[e], u, kDefer ? S[i][e] : al[e] * S[i][e]);
+      for (int e = 0; e < EPL; ++e) S[i][e] = fmaf(bk[e], u, S[i][e]);
     }
   }
 
