@@ -150,9 +150,18 @@ def test_ragged_grid_not_multiple_of_8(torch_cuda):
     print(stats)
 
 
-def test_long_requests(torch_cuda):
-    cfg = small(B=3, H_=2, HV=4, tokens="u:40..64", gate=wl.LOWER_BOUND, lb=-5.0, seed=9)
-    _say("long", cfg)
+@pytest.mark.parametrize("gate", [wl.LOWER_BOUND, wl.SOFTPLUS])
+@pytest.mark.parametrize("layout,sdt", [("k_first", "f32"), ("v_first", "f32"),
+                                        ("k_first", "bf16"), ("v_first", "bf16")])
+def test_long_requests(torch_cuda, gate, layout, sdt):
+    """Requests of 40 to 64 tokens: the kernels' deferred decay folds each
+    key's pending factor into the slab several times within a request (a
+    lower-bound gate of -5 takes it below 2^-64 in about nine tokens, the
+    drawn softplus gates in fewer)."""
+    cfg = small(B=3, H_=2, HV=4, tokens="u:40..64", gate=gate,
+                lb=-5.0 if gate == wl.LOWER_BOUND else 0.0, seed=9, state_layout=layout,
+                state_dtype=sdt)
+    _say("long", gate, layout, sdt)
     stats, _, _ = H.parity_case(wl.draw(cfg))
     print(stats)
 
