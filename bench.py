@@ -3,6 +3,13 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
     python bench.py --prefill [--matmul split_bf16|f32]
 
+Compute-heavy launches (the chunked prefill, multi-token decode batches on a
+bf16 pool) run back to back show a power transient: the second launch is
+~35% slower than the first and the time settles over about 30 launches.
+So the default warmup is 40 launches for --prefill and for workloads with
+more than one token per request, 5 otherwise (the one-token batches are
+bound by HBM and show no transient).
+
 A step is one kda_decode call over one batch of the workload (default: the
 96-head layer, B=256 requests x 1 token, dk = dv = 128, bf16 q/k/v, fp32
 state pool of 512 slots).  All inputs are resident in HBM before timing.
@@ -290,7 +297,10 @@ def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed launches first (default 5; 40 for --prefill and for "
+                         "workloads with more than one token per request, whose launches "
+                         "show a power transient that settles over about 30 of them)")
     ap.add_argument("--workload", default=None)
     ap.add_argument("--state-layout", choices=("k_first", "v_first"), default=None,
                     help="default: the workload's (key-first for the decode batches)")
@@ -331,6 +341,8 @@ def main(argv=None) -> int:
         over["lower_bound"] = -5.0 if args.gate == "lower_bound" else 0.0
     cfg = wl.preset(name, **over)
     log(f"[bench] workload {name}: {cfg.description}" + (f" (overrides {over})" if over else ""))
+    if args.warmup is None:
+        args.warmup = 40 if (args.prefill or cfg.tokens != "1") else 5
     inp = wl.draw(cfg)
     # the oracle workers fork here, before anything touches the GPU (the
     # conv step has no oracle baseline of its own here)
