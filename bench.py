@@ -4,8 +4,10 @@
     python bench.py --prefill [--matmul split_bf16|f32]
 
 Compute-heavy launches (the chunked prefill, multi-token decode batches on a
-bf16 pool) run back to back show a power transient: the second launch is
-~35% slower than the first and the time settles over about 30 launches.
+bf16 pool) run back to back show a transient: the second launch is ~35%
+slower than the first and the time settles over about 30 launches (the
+pattern of the chip's clock and power management adjusting to the load;
+the one-token batches, bound by HBM, do not show it).
 So the default warmup is 40 launches for --prefill and for workloads with
 more than one token per request, 5 otherwise (the one-token batches are
 bound by HBM and show no transient).
@@ -300,7 +302,7 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=None,
                     help="untimed launches first (default 5; 40 for --prefill and for "
                          "workloads with more than one token per request, whose launches "
-                         "show a power transient that settles over about 30 of them)")
+                         "show a slow-down transient that settles over about 30 of them)")
     ap.add_argument("--workload", default=None)
     ap.add_argument("--state-layout", choices=("k_first", "v_first"), default=None,
                     help="default: the workload's (key-first for the decode batches)")
