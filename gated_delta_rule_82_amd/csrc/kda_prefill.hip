@@ -280,11 +280,21 @@ __device__ __forceinline__ void mma_identity(f32x4& acc, const float (&a)[N], in
   }
 }
 
-// Two state accumulator tiles as one K = 32 operand; the state stays live.
+// Two state accumulator tiles as one K = 32 operand, and the same tiles
+// decayed in that pass (row i of tile lo by elo[i], of tile hi by ehi[i]).
+// The decayed values go to new registers, so the undecayed ones die at the
+// split and their remainders come from the in-place dot product (one
+// instruction each) instead of a widening shift or mask and a subtraction.
 template <int PREC>
-__device__ __forceinline__ Frag<PREC, 8> acc_frag8(const f32x4& lo, const f32x4& hi) {
+__device__ __forceinline__ Frag<PREC, 8> acc_frag8_decay(f32x4& lo, f32x4& hi, const f32x4& elo,
+                                                         const f32x4& ehi) {
   const float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return make_frag<PREC, 8, true>(v);
+  lo *= elo;
+  hi *= ehi;
+  // keeps the products here: sunk to the state update, they would keep the
+  // undecayed values live past the split
+  asm volatile("" : "+v"(lo), "+v"(hi));
+  return make_frag<PREC, 8>(v);
 }
 
 template <int PREC>
@@ -554,6 +564,21 @@ __device__ __forceinline__ void solve_rows(float (&tc)[J], const float (&nlt)[kC
 // LDS of one workgroup
 // ---------------------------------------------------------------------------
 
+// Sum of a token's NW per-wave partials (a row of NW floats padded to a
+// multiple of four), started from the first partial: 0 + x is not folded
+// away for floats, so a zero start would cost an addition.
+template <int NW>
+__device__ __forceinline__ float wave_sum(const float* row) {
+  float s = 0.0f;
+#pragma unroll
+  for (int w4 = 0; w4 < NW; w4 += 4) {
+    const f32x4 p4 = *reinterpret_cast<const f32x4*>(row + w4);
+#pragma unroll
+    for (int ww = 0; ww < 4 && w4 + ww < NW; ++ww) s = w4 + ww == 0 ? p4[0] : s + p4[ww];
+  }
+  return s;
+}
+
 template <int DK, int NW, int PREC>
 struct alignas(16) ChunkShared {
   static constexpr int NWP = (NW + 3) / 4 * 4;   // norm partials per token, padded
@@ -598,24 +623,27 @@ struct ChunkInputs {
 // Per-token log2-decays of N channels, log2(e) g: the softplus form
 // -exp(A_log) softplus(x + dt_bias), or the lower-bound form
 // lb sigmoid(exp(A_log) (x + dt_bias)) = lb / (1 + exp(-z)) with
-// exp(-z) = exp2(-z log2(e)); zero for a padding token.  The softplus is
+// exp(-z) = exp2(-z log2(e)); zero for a padding token.  The bias comes in
+// the form the gate takes it: dt_bias for the softplus, -dt_bias exp(A_log)
+// log2(e) for the lower bound (whose exponent is then one fused multiply-add
+// of the pre-activation).  The softplus is
 // taken in base 2, log2(e) softplus(z) = log2(e) max(z, 0) +
 // log2(1 + 2^(-|z| log2(e))): the decay factor exp(g) only sees the
 // absolute error of g, which here is about exp(A_log) * 1e-7 (the rounding
 // of 1 + 2^(...)) at most, as for the softplus with the corrected log1p.
 template <int N>
 __device__ __forceinline__ void log2_decays(int gate_mode, float amp, float amp2, float lb2, bool live,
-                                            const float (&x)[N], const float (&dtb)[N], float (&G)[N]) {
+                                            const float (&x)[N], const float (&bias)[N], float (&G)[N]) {
   if (gate_mode == KDA_GATE_SOFTPLUS) {     // uniform branch
 #pragma unroll
     for (int j = 0; j < N; ++j) {
-      const float z = x[j] + dtb[j];
+      const float z = x[j] + bias[j];
       const float l = __builtin_amdgcn_logf(1.0f + exp2_f(-kLog2e * fabsf(z)));   // log2
       G[j] = -fmaf(amp2, fmaxf(z, 0.0f), amp * l);
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < N; ++j) G[j] = lb2 * __builtin_amdgcn_rcpf(1.0f + exp2_f(-amp2 * (x[j] + dtb[j])));
+    for (int j = 0; j < N; ++j) G[j] = lb2 * __builtin_amdgcn_rcpf(1.0f + exp2_f(fmaf(-amp2, x[j], bias[j])));
   }
 #pragma unroll
   for (int j = 0; j < N; ++j) G[j] = live ? G[j] : 0.0f;
@@ -881,6 +909,13 @@ kda_prefill_chunks(DecodeArgs a) {
 
   // channel groups of this wave: group w + NW p covers channels
   // [CGS (w + NW p), +CGS); this lane's CPL start at chan0[p]
+  // gates are carried in base-2 units, G2 = G log2(e), so that every
+  // exp(.) of them is one exp2 instruction
+  const float amp = exp_f(a.a_log[hv]);
+  const float amp2 = amp * kLog2e;
+  const float lb2 = a.lower_bound * kLog2e;
+  // the gate bias of the lane's channels, in the form log2_decays takes
+  const bool lb_gate = a.gate_mode != KDA_GATE_SOFTPLUS;
   float dtb[NP][CPL];
   int chan0[NP];
 #pragma unroll
@@ -888,14 +923,11 @@ kda_prefill_chunks(DecodeArgs a) {
     const int gi = w + NW * p;
     chan0[p] = CGS * gi + CPL * g;
 #pragma unroll
-    for (int j = 0; j < CPL; ++j)
-      dtb[p][j] = gi < NG ? a.dt_bias[static_cast<int64_t>(hv) * DK + chan0[p] + j] : 0.0f;
+    for (int j = 0; j < CPL; ++j) {
+      const float bj = gi < NG ? a.dt_bias[static_cast<int64_t>(hv) * DK + chan0[p] + j] : 0.0f;
+      dtb[p][j] = lb_gate ? -amp2 * bj : bj;
+    }
   }
-  // gates are carried in base-2 units, G2 = G log2(e), so that every
-  // exp(.) of them is one exp2 instruction
-  const float amp = exp_f(a.a_log[hv]);
-  const float amp2 = amp * kLog2e;
-  const float lb2 = a.lower_bound * kLog2e;
 
   // Loads are unconditional (a token past the request's end reads the
   // request's last row and is zeroed where it is used), so the compiler can
@@ -1148,38 +1180,17 @@ kda_prefill_chunks(DecodeArgs a) {
       const f32x4 bt = *reinterpret_cast<const f32x4*>(&sh.beta[4 * g]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float s2 = 0.0f;
-#pragma unroll
-        for (int w4 = 0; w4 < NW; w4 += 4) {
-          const f32x4 pk4 = *reinterpret_cast<const f32x4*>(&sh.nk[4 * g + i][w4]);
-#pragma unroll
-          for (int ww = 0; ww < 4 && w4 + ww < NW; ++ww) s2 += pk4[ww];
-        }
-        rk[i] = rsqrt_f(s2 + a.l2_eps);
+        rk[i] = rsqrt_f(wave_sum<NW>(&sh.nk[4 * g + i][0]) + a.l2_eps);
         br[i] = bt[i] * rk[i];
       }
     }
-    float rkn, rqn;
-    {
-      float s2k = 0.0f, s2q = 0.0f;
-#pragma unroll
-      for (int w4 = 0; w4 < NW; w4 += 4) {
-        const f32x4 pk4 = *reinterpret_cast<const f32x4*>(&sh.nk[n][w4]);
-        const f32x4 pq4 = *reinterpret_cast<const f32x4*>(&sh.nq[n][w4]);
-#pragma unroll
-        for (int ww = 0; ww < 4 && w4 + ww < NW; ++ww) {
-          s2k += pk4[ww];
-          s2q += pq4[ww];
-        }
-      }
-      rkn = rsqrt_f(s2k + a.l2_eps);
-      rqn = a.scale * rsqrt_f(s2q + a.l2_eps);
-    }
+    const float rkn = rsqrt_f(wave_sum<NW>(&sh.nk[n][0]) + a.l2_eps);
+    const float rqn = a.scale * rsqrt_f(wave_sum<NW>(&sh.nq[n][0]) + a.l2_eps);
     // -L[t][s] for rows t = 4g + i, column s = n, into the wave's copy
     {
-      f32x4 Pf = {0.0f, 0.0f, 0.0f, 0.0f};
+      f32x4 Pf = *reinterpret_cast<const f32x4*>(&sh.pp[0][n][4 * g]);
 #pragma unroll
-      for (int ww = 0; ww < NW; ++ww) Pf += *reinterpret_cast<const f32x4*>(&sh.pp[ww][n][4 * g]);
+      for (int ww = 1; ww < NW; ++ww) Pf += *reinterpret_cast<const f32x4*>(&sh.pp[ww][n][4 * g]);
       const float cs = rkn * sh.beta[n];
 #pragma unroll
       for (int i = 0; i < 4; ++i) sh.nl[w][4 * g + i][n] = n < 4 * g + i ? -(rk[i] * cs * Pf[i]) : 0.0f;
@@ -1207,9 +1218,9 @@ kda_prefill_chunks(DecodeArgs a) {
     // R_raw as the B operand of R_raw^T: lane (t = n, g) holds R[t][4g + j]
     float rv[4];
     {
-      f32x4 Rf = {0.0f, 0.0f, 0.0f, 0.0f};
+      f32x4 Rf = *reinterpret_cast<const f32x4*>(&sh.rr[0][n][4 * g]);
 #pragma unroll
-      for (int ww = 0; ww < NW; ++ww) Rf += *reinterpret_cast<const f32x4*>(&sh.rr[ww][n][4 * g]);
+      for (int ww = 1; ww < NW; ++ww) Rf += *reinterpret_cast<const f32x4*>(&sh.rr[ww][n][4 * g]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) rv[j] = 4 * g + j <= n ? Rf[j] : 0.0f;
     }
@@ -1222,9 +1233,13 @@ kda_prefill_chunks(DecodeArgs a) {
     for (int s = 0; s < KS; ++s) {
       const Frag<PREC, 8> fk = sh.kt.frag8(n, s, g);
       const Frag<PREC, 8> fq = sh.qt.frag8(n, s, g);
+      // exp(Gamma_last) of the two tiles' rows: S = diag(exp(Gamma_last)) S
+      // is applied here, on the way to the operands
+      const f32x4 e0 = *reinterpret_cast<const f32x4*>(&sh.egl[32 * s + 4 * g]);
+      const f32x4 e1 = *reinterpret_cast<const f32x4*>(&sh.egl[32 * s + 16 + 4 * g]);
 #pragma unroll
       for (int nt = 0; nt < NTV; ++nt) {
-        const Frag<PREC, 8> fs = acc_frag8<PREC>(S[2 * s][nt], S[2 * s + 1][nt]);
+        const Frag<PREC, 8> fs = acc_frag8_decay<PREC>(S[2 * s][nt], S[2 * s + 1][nt], e0, e1);
         mma(X[nt], fk, fs);
         mma(YT[nt], fs, fq);
       }
@@ -1266,14 +1281,9 @@ kda_prefill_chunks(DecodeArgs a) {
     }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const f32x4 e = *reinterpret_cast<const f32x4*>(&sh.egl[16 * mt + 4 * g]);
       const Frag<PREC, 4> fk = sh.kup.frag4(16 * mt + n, g);
 #pragma unroll
-      for (int nt = 0; nt < NTV; ++nt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) S[mt][nt][i] *= e[i];
-        mma(S[mt][nt], fk, fu[nt]);
-      }
+      for (int nt = 0; nt < NTV; ++nt) mma(S[mt][nt], fk, fu[nt]);
     }
     lds_barrier();   // the shared tables are rewritten by the next chunk
   }
