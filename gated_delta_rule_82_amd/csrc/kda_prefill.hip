@@ -95,7 +95,12 @@ namespace kda {
 namespace {
 
 constexpr int kChunk = 16;          // tokens per chunk: one MFMA M / K tile
-constexpr int kSlabCols = 32;       // value columns per wave (two MFMA N tiles)
+// Value columns per wave: 32 (two MFMA N tiles), one workgroup of four
+// waves per 128-column tile, when the batch fills the chip; 16 (one tile),
+// two workgroups per tile, each with four waves and half the columns, when
+// it does not (each workgroup then runs the whole elementwise stage).
+constexpr int kSlabCols = 32;
+constexpr int kNarrowSlabCols = 16;
 constexpr int kGroupChannels = 32;  // key channels per elementwise channel group
 constexpr float kSafeSpan = 120.0f; // largest decay span of the one-product P, R
 // The table factors exp(Gamma_t) and exp(Gamma_last - Gamma_t) use
@@ -579,7 +584,7 @@ __device__ __forceinline__ float wave_sum(const float* row) {
   return s;
 }
 
-template <int DK, int NW, int PREC>
+template <int DK, int NW, int PREC, int CGS>
 struct alignas(16) ChunkShared {
   static constexpr int NWP = (NW + 3) / 4 * 4;   // norm partials per token, padded
   // published by every wave for its channels, read by all after the barrier
@@ -596,8 +601,8 @@ struct alignas(16) ChunkShared {
   // or between that barrier and the last (-L), never both.
   union {
     struct {                      // private to each wave: the exact decay sums
-      float pg[NW][kChunk][kGroupChannels + 4];   // of its channel group (prefix
-      float ps[NW][kChunk][kGroupChannels + 4];   // sums of integer parts, of remainders)
+      float pg[NW][kChunk][CGS + 4];   // of its channel group (prefix sums
+      float ps[NW][kChunk][CGS + 4];   // of integer parts, of remainders)
     };
     float nl[NW][kChunk][kPT];    // -L: [t][s], each wave its own copy
   };
@@ -607,12 +612,12 @@ struct alignas(16) ChunkShared {
 // the gate pre-activation of token lane % 16 at a quarter of the group's
 // channels; a quarter of the value slab's columns and the beta logit of that
 // token.
-template <int NP, bool QBF16>
+template <int NP, bool QBF16, int CGS, int VC>
 struct ChunkInputs {
-  static constexpr int CPL = kGroupChannels / 4;
+  static constexpr int CPL = CGS / 4;
   RunN<QBF16, CPL> q[NP], k[NP];
   RunN<false, CPL> x[NP];
-  RunN<QBF16, kSlabCols / 4> v;
+  RunN<QBF16, VC / 4> v;
   float bl;
 };
 
@@ -825,26 +830,29 @@ __device__ int head_by_decay_rank(const float* a_log, int HV, int r, int lane) {
 constexpr int kOrderMinTokens = 64;
 constexpr int kOrderMaxHeads = 1024;
 
-// At dv = 128, two workgroups per CU (at most 256 registers per lane, two
-// 70 KiB LDS footprints in 160 KiB): the chunk step is VALU- and
-// latency-bound at one wave per SIMD, and a second workgroup's waves fill
-// the gaps.
-constexpr int prefill_blocks_per_cu(int dv) { return dv == 128 ? 2 : 1; }
+// At dv = 128 with 32-column slabs, two workgroups per CU (at most 256
+// registers per lane, two 57 KiB LDS footprints in 160 KiB): the chunk step
+// is VALU- and latency-bound at one wave per SIMD, and a second
+// workgroup's waves fill the gaps.
+constexpr int prefill_blocks_per_cu(int dv, int vc) { return dv == 128 && vc == kSlabCols ? 2 : 1; }
 
-template <int DK, int DV, bool QBF16, bool SBF16, bool VFIRST, int PREC>
-__global__ void __launch_bounds__(DV / kSlabCols * kWave, prefill_blocks_per_cu(DV))
+// Workgroups per (request, value head) tile: two with 16-column slabs.
+constexpr int prefill_tile_groups(int vc) { return vc == kNarrowSlabCols ? 2 : 1; }
+
+template <int DK, int DV, bool QBF16, bool SBF16, bool VFIRST, int PREC, int VC>
+__global__ void __launch_bounds__(DV / VC / prefill_tile_groups(VC) * kWave, prefill_blocks_per_cu(DV, VC))
 kda_prefill_chunks(DecodeArgs a) {
-  constexpr int VC = kSlabCols;
+  constexpr int NWG = prefill_tile_groups(VC);
   constexpr int NTV = VC / 16;           // value tiles per wave
   constexpr int VPL = VC / 4;            // value columns per lane in the V operand
-  constexpr int NW = DV / VC;            // waves: one VC-value slab each
+  constexpr int NW = DV / VC / NWG;      // waves: one VC-value slab each
   constexpr int CGS = kGroupChannels;
   constexpr int CPL = CGS / 4;           // channels per lane in the elementwise stage
   constexpr int NG = DK / CGS;           // channel groups
   constexpr int NP = (NG + NW - 1) / NW; // channel group passes per wave
   constexpr int MT = DK / 16;            // state row tiles
   constexpr int KS = DK / 32;            // K = 32 steps over the channels
-  using Shared = ChunkShared<DK, NW, PREC>;
+  using Shared = ChunkShared<DK, NW, PREC, CGS>;
 
   __shared__ Shared sh;
 
@@ -853,14 +861,17 @@ kda_prefill_chunks(DecodeArgs a) {
   const int n = lane % 16;               // token / accumulator column
   const int g = lane / 16;               // channel quarter / accumulator row group
 
+  // the workgroup's tile, and its part of the tile's value columns
+  const uint32_t tile_id = blockIdx.x / NWG;
+  const int part = static_cast<int>(blockIdx.x % NWG);
   int b, hv;
   if (a.gate_mode == KDA_GATE_SOFTPLUS && a.HV > 1 && a.HV <= kOrderMaxHeads &&
       a.T / kOrderMinTokens >= a.B) {   // uniform
-    b = static_cast<int>(blockIdx.x % static_cast<uint32_t>(a.B));
-    hv = head_by_decay_rank(a.a_log, a.HV, static_cast<int>(blockIdx.x / static_cast<uint32_t>(a.B)), lane);
+    b = static_cast<int>(tile_id % static_cast<uint32_t>(a.B));
+    hv = head_by_decay_rank(a.a_log, a.HV, static_cast<int>(tile_id / static_cast<uint32_t>(a.B)), lane);
   } else {
-    b = static_cast<int>(blockIdx.x / static_cast<uint32_t>(a.HV));
-    hv = static_cast<int>(blockIdx.x) - b * a.HV;
+    b = static_cast<int>(tile_id / static_cast<uint32_t>(a.HV));
+    hv = static_cast<int>(tile_id) - b * a.HV;
   }
   const int h = hv / a.G;
   int t0 = a.cu_seqlens[b];
@@ -869,7 +880,7 @@ kda_prefill_chunks(DecodeArgs a) {
   t1 = t1 < t0 ? t0 : (t1 > a.T ? a.T : t1);
   if (t1 == t0) return;
   const int slot = a.state_indices[b];
-  const int vcol0 = VC * w;
+  const int vcol0 = VC * (NW * part + w);
 
   if (slot < 0 || slot >= a.N) {   // skipped request: zero rows, no state access
     for (int t = t0; t < t1; ++t)
@@ -932,7 +943,7 @@ kda_prefill_chunks(DecodeArgs a) {
   // Loads are unconditional (a token past the request's end reads the
   // request's last row and is zeroed where it is used), so the compiler can
   // count them exactly and never waits for more than the oldest in flight.
-  auto load_inputs = [&](ChunkInputs<NP, QBF16>& in, int c0) {
+  auto load_inputs = [&](ChunkInputs<NP, QBF16, CGS, VC>& in, int c0) {
     const int64_t tok = c0 + n < t1 ? c0 + n : t1 - 1;
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
@@ -950,7 +961,7 @@ kda_prefill_chunks(DecodeArgs a) {
   // One input buffer: each chunk first takes its inputs out of it (q, k
   // and the gate unpacked, v and beta kept), then refills it with the next
   // chunk's, which stay in flight while this chunk is processed.
-  ChunkInputs<NP, QBF16> in;
+  ChunkInputs<NP, QBF16, CGS, VC> in;
   load_inputs(in, t0);
   // every load so far (state, first inputs) completes here, outside the
   // loop, so the loop's waits only cover the previous chunk's prefetch
@@ -1312,20 +1323,35 @@ kda_prefill_chunks(DecodeArgs a) {
 
 // The launch's own status decides KDA_ERR_LAUNCH (hipGetLastError could
 // also report an earlier, unrelated error of the calling thread).
-template <int DK, int DV, bool QBF16, bool SBF16, bool VFIRST, int PREC>
+template <int DK, int DV, bool QBF16, bool SBF16, bool VFIRST, int PREC, int VC>
 int launch_one(const DecodeArgs& a, hipStream_t stream) {
-  const int64_t grid = static_cast<int64_t>(a.B) * a.HV;
+  constexpr int NWG = prefill_tile_groups(VC);
+  const int64_t grid = static_cast<int64_t>(a.B) * a.HV * NWG;
   void* kargs[] = {const_cast<DecodeArgs*>(&a)};
   const hipError_t rc =
-      hipLaunchKernel(reinterpret_cast<const void*>(&kda_prefill_chunks<DK, DV, QBF16, SBF16, VFIRST, PREC>),
-                      dim3(static_cast<uint32_t>(grid)), dim3(DV / kSlabCols * kWave), kargs, 0, stream);
+      hipLaunchKernel(reinterpret_cast<const void*>(&kda_prefill_chunks<DK, DV, QBF16, SBF16, VFIRST, PREC, VC>),
+                      dim3(static_cast<uint32_t>(grid)), dim3(DV / VC / NWG * kWave), kargs, 0, stream);
   return rc == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+// Tiles up to which a dv = 128 batch takes 16-column slabs in two
+// workgroups per tile: with at most one tile per two CUs, the second
+// workgroup runs on an otherwise idle CU, and each wave's chunk step is
+// shorter by half a slab's products.
+constexpr int64_t kNarrowMaxTiles = 128;
+
+template <int DK, int DV, bool QBF16, bool SBF16, bool VFIRST, int PREC>
+int pick_slab(const DecodeArgs& a, hipStream_t s) {
+  if constexpr (DV == 128)
+    if (static_cast<int64_t>(a.B) * a.HV <= kNarrowMaxTiles)
+      return launch_one<DK, DV, QBF16, SBF16, VFIRST, PREC, kNarrowSlabCols>(a, s);
+  return launch_one<DK, DV, QBF16, SBF16, VFIRST, PREC, kSlabCols>(a, s);
 }
 
 template <int DK, int DV, bool QBF16, bool SBF16, bool VFIRST>
 int pick_prec(const DecodeArgs& a, int prec, hipStream_t s) {
-  return prec == KDA_MATMUL_F32 ? launch_one<DK, DV, QBF16, SBF16, VFIRST, KDA_MATMUL_F32>(a, s)
-                                : launch_one<DK, DV, QBF16, SBF16, VFIRST, KDA_MATMUL_SPLIT_BF16>(a, s);
+  return prec == KDA_MATMUL_F32 ? pick_slab<DK, DV, QBF16, SBF16, VFIRST, KDA_MATMUL_F32>(a, s)
+                                : pick_slab<DK, DV, QBF16, SBF16, VFIRST, KDA_MATMUL_SPLIT_BF16>(a, s);
 }
 
 template <int DK, int DV>

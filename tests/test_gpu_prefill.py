@@ -85,6 +85,30 @@ def test_prefill_every_specialization(torch_cuda, dk, dv, layout, sdt, qkv, matm
     print("spec", dk, dv, layout, sdt, qkv, matmul, stats, flush=True)
 
 
+# dv = 128 batches of at most 128 (request, head) tiles run each tile as two
+# workgroups of 16-column slabs (every case above); larger ones as one
+# workgroup of 32-column slabs.  These cases put the larger form through
+# ragged chunks, both gates, both layouts and a bf16 pool; the first sits
+# one tile past the switch.
+WIDE_GRID = {
+    "grid129_vfirst": work("grid129_vfirst", B=3, H_=43, HV=43, DK=128, DV=128, tokens="u:1..60", seed=12,
+                           state_layout="v_first"),
+    "grid160_kfirst_softplus_gqa": work("grid160_kfirst_softplus_gqa", B=5, H_=16, HV=32, DK=128, DV=128,
+                                        tokens="u:1..70", gate=wl.SOFTPLUS, seed=13),
+    "grid144_bf16_state": work("grid144_bf16_state", B=4, H_=36, HV=36, DK=128, DV=128, tokens="u:0..50",
+                               seed=14, state_dtype="bf16", state_layout="v_first", qkv="f32"),
+}
+
+
+@pytest.mark.parametrize("matmul", MATMULS)
+@pytest.mark.parametrize("name", sorted(WIDE_GRID))
+def test_prefill_wide_grid(torch_cuda, name, matmul):
+    cfg = WIDE_GRID[name]
+    _say("prefill wide grid", name, matmul, cfg)
+    stats, _, _ = H.parity_case(wl.draw(cfg), entry="prefill", matmul=matmul)
+    print(name, matmul, stats, flush=True)
+
+
 @pytest.mark.parametrize("matmul", MATMULS)
 def test_prefill_long_request(torch_cuda, matmul):
     """One 6000-token request (375 chunks): the error must not grow with length."""
