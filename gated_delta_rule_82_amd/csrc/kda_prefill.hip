@@ -313,11 +313,18 @@ __device__ __forceinline__ Frag<PREC, 4> acc_frag4(const f32x4& x) {
 // are written 8 channels at a time and read as K = 32 slices in the order of
 // two stacked accumulator tiles: value j of lane group g is channel
 // 32s + 16 (j / 4) + 4g + j % 4.
-template <int PREC, int DK>
+//
+// The LDS tables (this one, KupTable, ChunkShared) take a KERNEL parameter
+// that differs between kernels, so no kernel shares their member functions
+// with another.  A member function shared by several kernels is optimized
+// once on its own, where `this` is a generic pointer, and only then inlined:
+// the kernels then carried 64-bit generic address arithmetic for the table
+// accesses (the 96-head prefill kernel spilled a register that way).
+template <int PREC, int DK, int KERNEL>
 struct RowTable;
 
-template <int DK>
-struct RowTable<KDA_MATMUL_F32, DK> {
+template <int DK, int KERNEL>
+struct RowTable<KDA_MATMUL_F32, DK, KERNEL> {
   static constexpr int P = DK + 4;
   float v[kChunk][P];
   template <int N>
@@ -339,8 +346,8 @@ struct RowTable<KDA_MATMUL_F32, DK> {
   }
 };
 
-template <int DK>
-struct RowTable<KDA_MATMUL_SPLIT_BF16, DK> {
+template <int DK, int KERNEL>
+struct RowTable<KDA_MATMUL_SPLIT_BF16, DK, KERNEL> {
   static constexpr int P = DK + 8;
   __bf16 hi[kChunk][P];
   __bf16 lo[kChunk][P];
@@ -368,11 +375,11 @@ struct RowTable<KDA_MATMUL_SPLIT_BF16, DK> {
 // consecutive tokens.  The split form keeps, per channel and group of four
 // tokens, the four hi parts and then the four lo parts: one 16-byte read is
 // the fragment as the matrix instruction takes it.
-template <int PREC, int DK>
+template <int PREC, int DK, int KERNEL>
 struct KupTable;
 
-template <int DK>
-struct KupTable<KDA_MATMUL_F32, DK> {
+template <int DK, int KERNEL>
+struct KupTable<KDA_MATMUL_F32, DK, KERNEL> {
   float v[DK][kPT];
   __device__ __forceinline__ void store(int d, int t, float x) { v[d][t] = x; }
   __device__ __forceinline__ Frag<KDA_MATMUL_F32, 4> frag4(int row, int g) const {
@@ -380,8 +387,8 @@ struct KupTable<KDA_MATMUL_F32, DK> {
   }
 };
 
-template <int DK>
-struct KupTable<KDA_MATMUL_SPLIT_BF16, DK> {
+template <int DK, int KERNEL>
+struct KupTable<KDA_MATMUL_SPLIT_BF16, DK, KERNEL> {
   static constexpr int P = kChunk / 4 * 8 + 8;   // bf16 per channel row, padded
   __bf16 v[DK][P];
   __device__ __forceinline__ void store(int d, int t, float x) {
@@ -584,13 +591,13 @@ __device__ __forceinline__ float wave_sum(const float* row) {
   return s;
 }
 
-template <int DK, int NW, int PREC, int CGS>
+template <int DK, int NW, int PREC, int CGS, int KERNEL>
 struct alignas(16) ChunkShared {
   static constexpr int NWP = (NW + 3) / 4 * 4;   // norm partials per token, padded
   // published by every wave for its channels, read by all after the barrier
-  RowTable<PREC, DK> kt;          // Kt_raw = k exp(Gamma)
-  RowTable<PREC, DK> qt;          // Qt_raw = q exp(Gamma)
-  KupTable<PREC, DK> kup;         // Kup_raw^T [channel][token] = k exp(Gamma_last - Gamma)
+  RowTable<PREC, DK, KERNEL> kt;  // Kt_raw = k exp(Gamma)
+  RowTable<PREC, DK, KERNEL> qt;  // Qt_raw = q exp(Gamma)
+  KupTable<PREC, DK, KERNEL> kup; // Kup_raw^T [channel][token] = k exp(Gamma_last - Gamma)
   float egl[DK];                  // exp(Gamma_last)
   float beta[kChunk];
   float nq[kChunk][NWP];          // per-wave partial sums of q^2, k^2 [token][wave]
@@ -798,7 +805,7 @@ __device__ __forceinline__ int order_key(float x) {
 // The value head of rank r when the HV heads are ordered by A_log, largest
 // first (ties by head index).  Keys form a total order, so the map from
 // rank to head is a permutation.  O(HV^2 / 64) per lane, once per wave.
-__device__ int head_by_decay_rank(const float* a_log, int HV, int r, int lane) {
+__device__ __forceinline__ int head_by_decay_rank(const float* a_log, int HV, int r, int lane) {
   int result = 0;
   for (int base = 0; base < HV; base += kWave) {
     const int h = base + lane;
@@ -852,7 +859,9 @@ kda_prefill_chunks(DecodeArgs a) {
   constexpr int NP = (NG + NW - 1) / NW; // channel group passes per wave
   constexpr int MT = DK / 16;            // state row tiles
   constexpr int KS = DK / 32;            // K = 32 steps over the channels
-  using Shared = ChunkShared<DK, NW, PREC, CGS>;
+  // the remaining template parameters, as the tables' per-kernel tag
+  constexpr int KERNEL = (QBF16 ? 1 : 0) + (SBF16 ? 2 : 0) + (VFIRST ? 4 : 0) + 8 * VC + 1024 * DV;
+  using Shared = ChunkShared<DK, NW, PREC, CGS, KERNEL>;
 
   __shared__ Shared sh;
 
