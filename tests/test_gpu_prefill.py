@@ -60,6 +60,11 @@ CASES = {
     "skip_and_empty": work("skip_and_empty", B=5, H_=2, HV=2, DK=64, DV=64,
                            cu_seqlens=(0, 20, 20, 41, 42, 42), state_indices=(3, 1, -1, 0, -1),
                            slots=6, seed=8),
+    # the same at dk = dv = 128 (two workgroups per tile, each zeroing its
+    # half of a skipped request's rows)
+    "skip_and_empty_d128": work("skip_and_empty_d128", B=5, H_=2, HV=2, DK=128, DV=128,
+                                cu_seqlens=(0, 20, 20, 41, 42, 42), state_indices=(3, 1, -1, 0, -1),
+                                slots=6, seed=15, state_layout="v_first"),
 }
 
 
