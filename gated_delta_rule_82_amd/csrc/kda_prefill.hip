@@ -548,26 +548,22 @@ __device__ __forceinline__ float cross_row_sum(float x) {
 // 16-lane row by the DPP broadcast inside the multiply-add itself (the
 // compiler would issue the broadcast as a move of its own).  Row 15 updates
 // nothing.  A DPP read needs two wait states after the VALU write of its
-// source: within a step the J columns go in order, so a column's next read
-// comes J - 1 >= 3 instructions after its write; before the first step, a
-// two-cycle nop covers the initial values.
+// source, and the compiler does not see the DPP inside the assembly: each
+// step opens with a two-cycle nop, whatever the compiler placed before it.
+// (Within a step the J columns go in order, so a column written by the
+// previous step is read J - 1 >= 3 instructions later anyway.)  Not
+// volatile: the steps only order by their data, so the compiler may
+// schedule independent work between them.
 template <int S, int J>
 __device__ __forceinline__ void solve_rows(float (&tc)[J], const float (&nlt)[kChunk]) {
-  static_assert(J == 4, "the wait-state argument above takes four columns");
+  static_assert(J == 4, "one step updates four columns");
   if constexpr (S < kChunk - 1) {
-    if constexpr (S == 0)
-      asm volatile("s_nop 1\n\t"
-                   "v_fmac_f32_dpp %0, %0, %4 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
-                   "v_fmac_f32_dpp %1, %1, %4 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
-                   "v_fmac_f32_dpp %2, %2, %4 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
-                   "v_fmac_f32_dpp %3, %3, %4 row_newbcast:0 row_mask:0xf bank_mask:0xf"
-                   : "+v"(tc[0]), "+v"(tc[1]), "+v"(tc[2]), "+v"(tc[3]) : "v"(nlt[S]));
-    else
-      asm volatile("v_fmac_f32_dpp %0, %0, %4 row_newbcast:%5 row_mask:0xf bank_mask:0xf\n\t"
-                   "v_fmac_f32_dpp %1, %1, %4 row_newbcast:%5 row_mask:0xf bank_mask:0xf\n\t"
-                   "v_fmac_f32_dpp %2, %2, %4 row_newbcast:%5 row_mask:0xf bank_mask:0xf\n\t"
-                   "v_fmac_f32_dpp %3, %3, %4 row_newbcast:%5 row_mask:0xf bank_mask:0xf"
-                   : "+v"(tc[0]), "+v"(tc[1]), "+v"(tc[2]), "+v"(tc[3]) : "v"(nlt[S]), "n"(S));
+    asm("s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %0, %4 row_newbcast:%5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %1, %4 row_newbcast:%5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %2, %4 row_newbcast:%5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %3, %4 row_newbcast:%5 row_mask:0xf bank_mask:0xf"
+        : "+v"(tc[0]), "+v"(tc[1]), "+v"(tc[2]), "+v"(tc[3]) : "v"(nlt[S]), "n"(S));
     solve_rows<S + 1, J>(tc, nlt);
   }
 }
