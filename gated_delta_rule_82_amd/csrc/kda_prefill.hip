@@ -166,10 +166,11 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // (first value in the lower half).  A remainder x - hi(x) is exact in fp32
 // (hi(x) is within a factor of two of x).
 //
-// Values that die at the split take the remainder with the bf16 dot product
-// instruction straight from the packed word, x + (-1) * hi(x): the builtin
-// selects the form that accumulates into x's register, one instruction per
-// value.  The selector words {-1, 0} and {0, -1} are passed through SGPRs:
+// The remainder comes from the bf16 dot product instruction straight from
+// the packed word, x + (-1) * hi(x): the builtin selects the form that
+// accumulates into x's register, one instruction per value, so x must die at
+// the split (the state, which lives on, is first decayed into new
+// registers; see acc_frag8_decay).  The selector words {-1, 0} and {0, -1} are passed through SGPRs:
 // the compiler encodes the first as the inline constant -1.0, which the
 // instruction does not read as that bf16 pair (the remainders of first
 // values came out wrong); from a register both selectors are exact.
@@ -186,22 +187,7 @@ __device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint3
   lo = __builtin_bit_cast(uint32_t, l);
 }
 
-// The same split for values that stay live (the state): the accumulating
-// dot product would need a copy of each, so hi(x) is widened from the packed
-// word with a shift or a mask and subtracted into a new register.  The word
-// is made opaque to the compiler, which otherwise converts the first value
-// again to widen it.
-__device__ __forceinline__ void split_pair_keep(float a, float b, uint32_t& hi, uint32_t& lo) {
-  const bf16x2 h = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
-  hi = __builtin_bit_cast(uint32_t, h);
-  asm("" : "+v"(hi));
-  const float ha = __builtin_bit_cast(float, hi << 16);
-  const float hb = __builtin_bit_cast(float, hi & 0xffff0000u);
-  const bf16x2 l = {static_cast<__bf16>(a - ha), static_cast<__bf16>(b - hb)};
-  lo = __builtin_bit_cast(uint32_t, l);
-}
-
-template <int PREC, int N, bool KEEP = false>
+template <int PREC, int N>
 __device__ __forceinline__ Frag<PREC, N> make_frag(const float (&x)[N]) {
   Frag<PREC, N> f;
   if constexpr (PREC == KDA_MATMUL_F32) {
@@ -211,10 +197,7 @@ __device__ __forceinline__ Frag<PREC, N> make_frag(const float (&x)[N]) {
     static_assert(N % 2 == 0, "split fragments hold pairs");
     uint32_t hi[N / 2], lo[N / 2];
 #pragma unroll
-    for (int j = 0; j < N / 2; ++j) {
-      if constexpr (KEEP) split_pair_keep(x[2 * j], x[2 * j + 1], hi[j], lo[j]);
-      else split_pair(x[2 * j], x[2 * j + 1], hi[j], lo[j]);
-    }
+    for (int j = 0; j < N / 2; ++j) split_pair(x[2 * j], x[2 * j + 1], hi[j], lo[j]);
     typedef typename Frag<PREC, N>::vec vec;
     f.hi = __builtin_bit_cast(vec, hi);
     f.lo = __builtin_bit_cast(vec, lo);
