@@ -90,11 +90,11 @@ def test_prefill_every_specialization(torch_cuda, dk, dv, layout, sdt, qkv, matm
     print("spec", dk, dv, layout, sdt, qkv, matmul, stats, flush=True)
 
 
-# dv = 128 batches of at most 128 (request, head) tiles run each tile as two
-# workgroups of 16-column slabs (every case above); larger ones as one
-# workgroup of 32-column slabs.  These cases put the larger form through
-# ragged chunks, both gates, both layouts and a bf16 pool; the first sits
-# one tile past the switch.
+# dv = 128 batches run in one of three forms by their number of (request,
+# head) tiles: up to 128 (every case above), two workgroups per tile with the
+# stage split; up to 256, one workgroup per tile with the split; more, one
+# plain workgroup per tile.  These cases put the larger forms through ragged
+# chunks, both gates, both layouts and a bf16 pool, each next to a switch.
 WIDE_GRID = {
     "grid129_vfirst": work("grid129_vfirst", B=3, H_=43, HV=43, DK=128, DV=128, tokens="u:1..60", seed=12,
                            state_layout="v_first"),
@@ -102,6 +102,12 @@ WIDE_GRID = {
                                         tokens="u:1..70", gate=wl.SOFTPLUS, seed=13),
     "grid144_bf16_state": work("grid144_bf16_state", B=4, H_=36, HV=36, DK=128, DV=128, tokens="u:0..50",
                                seed=14, state_dtype="bf16", state_layout="v_first", qkv="f32"),
+    "grid256_vfirst_softplus": work("grid256_vfirst_softplus", B=8, H_=32, HV=32, DK=128, DV=128,
+                                    tokens="u:1..40", gate=wl.SOFTPLUS, seed=16, state_layout="v_first"),
+    "grid257_kfirst": work("grid257_kfirst", B=1, H_=257, HV=257, DK=128, DV=128, tokens="37", seed=17),
+    "grid288_kfirst_softplus_bf16_state": work("grid288_kfirst_softplus_bf16_state", B=9, H_=16, HV=32,
+                                               DK=128, DV=128, tokens="u:1..40", gate=wl.SOFTPLUS, seed=18,
+                                               state_dtype="bf16"),
 }
 
 
