@@ -1403,18 +1403,27 @@ int launch_one(const DecodeArgs& a, hipStream_t stream) {
 //   2048-token requests over 96 heads: 382 us against 490 us);
 // - more: one plain workgroup per tile, two per CU, whose second workgroup
 //   fills the first's waits as the split would (eight 2048-token requests:
-//   the split measured 1.4% slower, 384 tiles 5.6% slower).
+//   the split measured 1.4% slower, 384 tiles 5.6% slower) -- except with
+//   fp32 q/k/v, whose prefetched inputs make the plain kernel spill 15-28
+//   registers where the split one spills 3-13 (eight 2048-token requests:
+//   1522 -> 1293 us with the split).
 constexpr int64_t kNarrowMaxTiles = 128;
 constexpr int64_t kSplitMaxTiles = 256;
 
 template <int DK, int DV, bool QBF16, bool SBF16, bool VFIRST, int PREC>
 int pick_slab(const DecodeArgs& a, hipStream_t s) {
-  if constexpr (DV == 128) {
+  if constexpr (DV != 128) {
+    return launch_one<DK, DV, QBF16, SBF16, VFIRST, PREC, kSlabCols, false>(a, s);
+  } else {
     const int64_t tiles = static_cast<int64_t>(a.B) * a.HV;
     if (tiles <= kNarrowMaxTiles) return launch_one<DK, DV, QBF16, SBF16, VFIRST, PREC, kNarrowSlabCols, true>(a, s);
-    if (tiles <= kSplitMaxTiles) return launch_one<DK, DV, QBF16, SBF16, VFIRST, PREC, kSlabCols, true>(a, s);
+    if constexpr (!QBF16) {
+      return launch_one<DK, DV, QBF16, SBF16, VFIRST, PREC, kSlabCols, true>(a, s);
+    } else {
+      return tiles <= kSplitMaxTiles ? launch_one<DK, DV, QBF16, SBF16, VFIRST, PREC, kSlabCols, true>(a, s)
+                                     : launch_one<DK, DV, QBF16, SBF16, VFIRST, PREC, kSlabCols, false>(a, s);
+    }
   }
-  return launch_one<DK, DV, QBF16, SBF16, VFIRST, PREC, kSlabCols, false>(a, s);
 }
 
 template <int DK, int DV, bool QBF16, bool SBF16, bool VFIRST>
