@@ -891,7 +891,7 @@ kda_prefill_chunks(DecodeArgs a) {
   const int g = lane / 16;               // channel quarter / accumulator row group
 
   // the workgroup's tile, and its part of the tile's value columns
-  const uint32_t tile_id = blockIdx.x / NWG;
+  const uint32_t tile_id = static_cast<uint32_t>(a.tile_base) + blockIdx.x / NWG;
   const int part = static_cast<int>(blockIdx.x % NWG);
   int b, hv;
   if (a.gate_mode == KDA_GATE_SOFTPLUS && a.HV > 1 && a.HV <= kOrderMaxHeads &&
@@ -1383,11 +1383,14 @@ kda_prefill_chunks(DecodeArgs a) {
 
 // The launch's own status decides KDA_ERR_LAUNCH (hipGetLastError could
 // also report an earlier, unrelated error of the calling thread).
+// Tiles [begin, end) of the batch, in the kernel's tile order.
 template <int DK, int DV, bool QBF16, bool SBF16, bool VFIRST, int PREC, int VC, bool SPLIT>
-int launch_one(const DecodeArgs& a, hipStream_t stream) {
+int launch_one(const DecodeArgs& args, int64_t begin, int64_t end, hipStream_t stream) {
   constexpr int NWG = prefill_tile_groups(VC);
-  const int64_t grid = static_cast<int64_t>(a.B) * a.HV * NWG;
-  void* kargs[] = {const_cast<DecodeArgs*>(&a)};
+  const int64_t grid = (end - begin) * NWG;
+  DecodeArgs a = args;
+  a.tile_base = static_cast<int32_t>(begin);
+  void* kargs[] = {&a};
   const hipError_t rc = hipLaunchKernel(
       reinterpret_cast<const void*>(&kda_prefill_chunks<DK, DV, QBF16, SBF16, VFIRST, PREC, VC, SPLIT>),
       dim3(static_cast<uint32_t>(grid)), dim3(DV / VC / NWG * kWave * (SPLIT ? 2 : 1)), kargs, 0, stream);
@@ -1401,27 +1404,45 @@ int launch_one(const DecodeArgs& a, hipStream_t stream) {
 //   plain workgroup per tile);
 // - up to 256: one workgroup per tile with the stage split, one per CU (two
 //   2048-token requests over 96 heads: 382 us against 490 us);
-// - more: one plain workgroup per tile, two per CU, whose second workgroup
-//   fills the first's waits as the split would (eight 2048-token requests:
-//   the split measured 1.4% slower, 384 tiles 5.6% slower) -- except with
-//   fp32 q/k/v, whose prefetched inputs make the plain kernel spill 15-28
-//   registers where the split one spills 3-13 (eight 2048-token requests:
-//   1522 -> 1293 us with the split).
-constexpr int64_t kNarrowMaxTiles = 128;
-constexpr int64_t kSplitMaxTiles = 256;
+// - more: plain workgroups, two per CU, whose second workgroup fills the
+//   first's waits as the split would (eight 2048-token requests: the split
+//   measured 1.4% slower, 384 tiles 5.6% slower).  When the tiles past the
+//   last full round of two per CU would leave three quarters of the CUs
+//   idle, they run as a second launch, two split-form workgroups per tile
+//   (six 2048-token requests over 96 heads, a tail of 64 tiles: 1098 ->
+//   1047 us).  A larger tail gains nothing from it (128 tiles: 1787 ->
+//   1788 us; 256: 1129 -> 1133 us): the plain launch starts its tail tiles
+//   as slots free up, the second launch only after the first has drained.
+//   With fp32 q/k/v, whose prefetched inputs make the plain kernel spill
+//   15-28 registers where the split one spills 3-13, every tile takes the
+//   split (eight 2048-token requests: 1522 -> 1293 us).
+constexpr int64_t kCUs = 256;   // MI355X
+constexpr int64_t kNarrowMaxTiles = kCUs / 2;
+constexpr int64_t kSplitMaxTiles = kCUs;
+constexpr int64_t kPlainRoundTiles = 2 * kCUs;
+constexpr int64_t kSplitTailMaxTiles = kCUs / 4;
 
 template <int DK, int DV, bool QBF16, bool SBF16, bool VFIRST, int PREC>
 int pick_slab(const DecodeArgs& a, hipStream_t s) {
+  const int64_t tiles = static_cast<int64_t>(a.B) * a.HV;
   if constexpr (DV != 128) {
-    return launch_one<DK, DV, QBF16, SBF16, VFIRST, PREC, kSlabCols, false>(a, s);
+    return launch_one<DK, DV, QBF16, SBF16, VFIRST, PREC, kSlabCols, false>(a, 0, tiles, s);
   } else {
-    const int64_t tiles = static_cast<int64_t>(a.B) * a.HV;
-    if (tiles <= kNarrowMaxTiles) return launch_one<DK, DV, QBF16, SBF16, VFIRST, PREC, kNarrowSlabCols, true>(a, s);
+    // a split-form launch over tiles [begin, end), at most kSplitMaxTiles
+    auto split = [&](int64_t begin, int64_t end) {
+      return end - begin <= kNarrowMaxTiles
+                 ? launch_one<DK, DV, QBF16, SBF16, VFIRST, PREC, kNarrowSlabCols, true>(a, begin, end, s)
+                 : launch_one<DK, DV, QBF16, SBF16, VFIRST, PREC, kSlabCols, true>(a, begin, end, s);
+    };
+    if (tiles <= kSplitMaxTiles) return split(0, tiles);
     if constexpr (!QBF16) {
-      return launch_one<DK, DV, QBF16, SBF16, VFIRST, PREC, kSlabCols, true>(a, s);
+      return launch_one<DK, DV, QBF16, SBF16, VFIRST, PREC, kSlabCols, true>(a, 0, tiles, s);
     } else {
-      return tiles <= kSplitMaxTiles ? launch_one<DK, DV, QBF16, SBF16, VFIRST, PREC, kSlabCols, true>(a, s)
-                                     : launch_one<DK, DV, QBF16, SBF16, VFIRST, PREC, kSlabCols, false>(a, s);
+      const int64_t tail = tiles % kPlainRoundTiles;
+      if (tail == 0 || tail > kSplitTailMaxTiles)
+        return launch_one<DK, DV, QBF16, SBF16, VFIRST, PREC, kSlabCols, false>(a, 0, tiles, s);
+      const int rc = launch_one<DK, DV, QBF16, SBF16, VFIRST, PREC, kSlabCols, false>(a, 0, tiles - tail, s);
+      return rc != KDA_OK ? rc : split(tiles - tail, tiles);
     }
   }
 }

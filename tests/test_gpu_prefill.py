@@ -108,6 +108,9 @@ WIDE_GRID = {
     "grid288_kfirst_softplus_bf16_state": work("grid288_kfirst_softplus_bf16_state", B=9, H_=16, HV=32,
                                                DK=128, DV=128, tokens="u:1..40", gate=wl.SOFTPLUS, seed=18,
                                                state_dtype="bf16"),
+    # 512 + 64 tiles: a plain launch for the first 512, a split one for the rest
+    "grid576_split_tail": work("grid576_split_tail", B=9, H_=64, HV=64, DK=128, DV=128, tokens="u:1..20",
+                               gate=wl.SOFTPLUS, seed=20),
     # fp32 q/k/v take the split at any tile count
     "grid260_f32_qkv": work("grid260_f32_qkv", B=4, H_=65, HV=65, DK=128, DV=128, tokens="u:1..30", seed=19,
                             qkv="f32", state_layout="v_first"),
