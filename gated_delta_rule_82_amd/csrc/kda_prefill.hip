@@ -890,6 +890,12 @@ kda_prefill_chunks(DecodeArgs a) {
   const int n = lane % 16;               // token / accumulator column
   const int g = lane / 16;               // channel quarter / accumulator row group
 
+  // With the split, the stage that bounds a chunk issues first when both of
+  // a SIMD's waves are ready: the products under the lower-bound gate, the
+  // elementwise stage (with its wide-span tiers) under the softplus.
+  if constexpr (SPLIT)
+    if (a.gate_mode == KDA_GATE_SOFTPLUS ? e_wave : p_wave) __builtin_amdgcn_s_setprio(1);
+
   // the workgroup's tile, and its part of the tile's value columns
   const uint32_t tile_id = static_cast<uint32_t>(a.tile_base) + blockIdx.x / NWG;
   const int part = static_cast<int>(blockIdx.x % NWG);
