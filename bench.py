@@ -565,11 +565,10 @@ def report_prefill(args, cfg, name, inp, cpu_pool, ms_per_step, mean_kernel_ms, 
     else:
         roof = dict(bound="mfma", **{k: matrix[k] for k in ("achieved", "peak", "unit", "frac")})
     roof["traffic"] = traffic
-    # the launch form the library takes for this many (request, head) tiles
-    # at dv = 128: two stage-split workgroups per tile (at most 128 tiles),
-    # one stage-split workgroup (at most 256), or one plain workgroup
+    # the launch form the library takes at dv = 128: the stage split, with
+    # two workgroups per tile up to 128 (request, head) tiles
     tiles = cfg.B * cfg.HV
-    form = ("" if cfg.DV != 128 or tiles > 256 else
+    form = ("" if cfg.DV != 128 else
             ",stage split, 2 workgroups per tile" if tiles <= 128 else ",stage split")
     roof["kernel"] = "kda_prefill_chunks<%d,%d,%s q/k/v,%s state,%s,%s%s>" % (
         cfg.DK, cfg.DV, cfg.qkv_dtype, cfg.state_dtype, cfg.state_layout.replace("_", ""),

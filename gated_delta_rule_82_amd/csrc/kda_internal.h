@@ -30,9 +30,6 @@ struct DecodeArgs {
   float* conv_win_v;            // [N, K-1, HV*dv] windows
   int32_t conv_k;               // K, 2..4
   int32_t conv_w_bf16;          // taps stored as bf16
-  // first (request, value head) tile of a prefill launch that covers only a
-  // range of the batch's tiles; 0 for a launch over all of them
-  int32_t tile_base;
 };
 
 // Arguments of the q/k convolution kernel of kda_decode_conv.

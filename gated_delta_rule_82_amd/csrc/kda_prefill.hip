@@ -842,13 +842,6 @@ __device__ __forceinline__ int head_by_decay_rank(const float* a_log, int HV, in
 constexpr int kOrderMinTokens = 64;
 constexpr int kOrderMaxHeads = 1024;
 
-// At dv = 128 without the stage split (below), two workgroups per CU (at
-// most 256 registers per lane, two 57 KiB LDS footprints in 160 KiB): the
-// chunk step is VALU- and latency-bound at one wave per SIMD, and a second
-// workgroup's waves fill the gaps.  With the split a workgroup is eight
-// waves and 99 KiB of LDS, one per CU.
-constexpr int prefill_blocks_per_cu(int dv, int vc) { return dv == 128 && vc == kSlabCols ? 2 : 1; }
-
 // Workgroups per (request, value head) tile: two with 16-column slabs.
 constexpr int prefill_tile_groups(int vc) { return vc == kNarrowSlabCols ? 2 : 1; }
 
@@ -856,11 +849,12 @@ constexpr int prefill_tile_groups(int vc) { return vc == kNarrowSlabCols ? 2 : 1
 // first half runs the elementwise stage of chunk c + 1 while the second half
 // runs the products of chunk c, the tables double-buffered between them, one
 // barrier per chunk; the halves share the SIMDs, so each stage's waits are
-// filled by the other's work.  Without it, every wave runs both stages of a
-// chunk in turn, with a barrier after each.
+// filled by the other's work.  At dv = 128 that is eight waves (at most 256
+// registers per lane, two waves per SIMD) and 99 KiB of LDS: one workgroup
+// per CU.  Without it, every wave runs both stages of a chunk in turn, with
+// a barrier after each.
 template <int DK, int DV, bool QBF16, bool SBF16, bool VFIRST, int PREC, int VC, bool SPLIT>
-__global__ void __launch_bounds__(DV / VC / prefill_tile_groups(VC) * kWave * (SPLIT ? 2 : 1),
-                                  SPLIT ? 1 : prefill_blocks_per_cu(DV, VC))
+__global__ void __launch_bounds__(DV / VC / prefill_tile_groups(VC) * kWave * (SPLIT ? 2 : 1), 1)
 kda_prefill_chunks(DecodeArgs a) {
   constexpr int NWG = prefill_tile_groups(VC);
   constexpr int NTV = VC / 16;           // value tiles per wave
@@ -897,7 +891,7 @@ kda_prefill_chunks(DecodeArgs a) {
     if (a.gate_mode == KDA_GATE_SOFTPLUS ? e_wave : p_wave) __builtin_amdgcn_s_setprio(1);
 
   // the workgroup's tile, and its part of the tile's value columns
-  const uint32_t tile_id = static_cast<uint32_t>(a.tile_base) + blockIdx.x / NWG;
+  const uint32_t tile_id = blockIdx.x / NWG;
   const int part = static_cast<int>(blockIdx.x % NWG);
   int b, hv;
   if (a.gate_mode == KDA_GATE_SOFTPLUS && a.HV > 1 && a.HV <= kOrderMaxHeads &&
@@ -1389,67 +1383,35 @@ kda_prefill_chunks(DecodeArgs a) {
 
 // The launch's own status decides KDA_ERR_LAUNCH (hipGetLastError could
 // also report an earlier, unrelated error of the calling thread).
-// Tiles [begin, end) of the batch, in the kernel's tile order.
 template <int DK, int DV, bool QBF16, bool SBF16, bool VFIRST, int PREC, int VC, bool SPLIT>
-int launch_one(const DecodeArgs& args, int64_t begin, int64_t end, hipStream_t stream) {
+int launch_one(const DecodeArgs& a, hipStream_t stream) {
   constexpr int NWG = prefill_tile_groups(VC);
-  const int64_t grid = (end - begin) * NWG;
-  DecodeArgs a = args;
-  a.tile_base = static_cast<int32_t>(begin);
-  void* kargs[] = {&a};
+  const int64_t grid = static_cast<int64_t>(a.B) * a.HV * NWG;
+  void* kargs[] = {const_cast<DecodeArgs*>(&a)};
   const hipError_t rc = hipLaunchKernel(
       reinterpret_cast<const void*>(&kda_prefill_chunks<DK, DV, QBF16, SBF16, VFIRST, PREC, VC, SPLIT>),
       dim3(static_cast<uint32_t>(grid)), dim3(DV / VC / NWG * kWave * (SPLIT ? 2 : 1)), kargs, 0, stream);
   return rc == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
-// dv = 128 batches by their number of (request, value head) tiles, which
-// decides how many CUs have work and how many workgroups each holds:
-// - up to 128: two workgroups per tile, 16-column slabs, the stage split
-//   (one 16 384-token prompt over 96 heads: 2.63 ms, against 3.80 ms as one
-//   plain workgroup per tile);
-// - up to 256: one workgroup per tile with the stage split, one per CU (two
-//   2048-token requests over 96 heads: 382 us against 490 us);
-// - more: plain workgroups, two per CU, whose second workgroup fills the
-//   first's waits as the split would (eight 2048-token requests: the split
-//   measured 1.4% slower, 384 tiles 5.6% slower).  When the tiles past the
-//   last full round of two per CU would leave three quarters of the CUs
-//   idle, they run as a second launch, two split-form workgroups per tile
-//   (six 2048-token requests over 96 heads, a tail of 64 tiles: 1098 ->
-//   1047 us).  A larger tail gains nothing from it (128 tiles: 1787 ->
-//   1788 us; 256: 1129 -> 1133 us): the plain launch starts its tail tiles
-//   as slots free up, the second launch only after the first has drained.
-//   With fp32 q/k/v, whose prefetched inputs make the plain kernel spill
-//   15-28 registers where the split one spills 3-13, every tile takes the
-//   split (eight 2048-token requests: 1522 -> 1293 us).
-constexpr int64_t kCUs = 256;   // MI355X
-constexpr int64_t kNarrowMaxTiles = kCUs / 2;
-constexpr int64_t kSplitMaxTiles = kCUs;
-constexpr int64_t kPlainRoundTiles = 2 * kCUs;
-constexpr int64_t kSplitTailMaxTiles = kCUs / 4;
+// dv = 128 batches take the stage split: with its bounding stage's waves
+// prioritized, one eight-wave workgroup per CU beats two plain four-wave
+// workgroups (eight 2048-token requests over 96 heads: 1132 -> 1087 us,
+// softplus 1328 -> 1291 us; 384 tiles 719 -> 679 us; 1536 tiles, three
+// full rounds of the plain form, 1096 -> 1105 us), and it spills less with
+// fp32 q/k/v.  Up to 128 tiles each tile is two workgroups of 16-column
+// slabs, so that twice as many CUs work (one 16 384-token prompt over 96
+// heads: 2.32 ms, against 3.80 ms as one plain workgroup per tile).
+constexpr int64_t kNarrowMaxTiles = 128;   // half of MI355X's 256 CUs
 
 template <int DK, int DV, bool QBF16, bool SBF16, bool VFIRST, int PREC>
 int pick_slab(const DecodeArgs& a, hipStream_t s) {
-  const int64_t tiles = static_cast<int64_t>(a.B) * a.HV;
   if constexpr (DV != 128) {
-    return launch_one<DK, DV, QBF16, SBF16, VFIRST, PREC, kSlabCols, false>(a, 0, tiles, s);
+    return launch_one<DK, DV, QBF16, SBF16, VFIRST, PREC, kSlabCols, false>(a, s);
   } else {
-    // a split-form launch over tiles [begin, end), at most kSplitMaxTiles
-    auto split = [&](int64_t begin, int64_t end) {
-      return end - begin <= kNarrowMaxTiles
-                 ? launch_one<DK, DV, QBF16, SBF16, VFIRST, PREC, kNarrowSlabCols, true>(a, begin, end, s)
-                 : launch_one<DK, DV, QBF16, SBF16, VFIRST, PREC, kSlabCols, true>(a, begin, end, s);
-    };
-    if (tiles <= kSplitMaxTiles) return split(0, tiles);
-    if constexpr (!QBF16) {
-      return launch_one<DK, DV, QBF16, SBF16, VFIRST, PREC, kSlabCols, true>(a, 0, tiles, s);
-    } else {
-      const int64_t tail = tiles % kPlainRoundTiles;
-      if (tail == 0 || tail > kSplitTailMaxTiles)
-        return launch_one<DK, DV, QBF16, SBF16, VFIRST, PREC, kSlabCols, false>(a, 0, tiles, s);
-      const int rc = launch_one<DK, DV, QBF16, SBF16, VFIRST, PREC, kSlabCols, false>(a, 0, tiles - tail, s);
-      return rc != KDA_OK ? rc : split(tiles - tail, tiles);
-    }
+    return static_cast<int64_t>(a.B) * a.HV <= kNarrowMaxTiles
+               ? launch_one<DK, DV, QBF16, SBF16, VFIRST, PREC, kNarrowSlabCols, true>(a, s)
+               : launch_one<DK, DV, QBF16, SBF16, VFIRST, PREC, kSlabCols, true>(a, s);
   }
 }
 

@@ -90,11 +90,11 @@ def test_prefill_every_specialization(torch_cuda, dk, dv, layout, sdt, qkv, matm
     print("spec", dk, dv, layout, sdt, qkv, matmul, stats, flush=True)
 
 
-# dv = 128 batches run in one of three forms by their number of (request,
-# head) tiles: up to 128 (every case above), two workgroups per tile with the
-# stage split; up to 256, one workgroup per tile with the split; more, one
-# plain workgroup per tile (with fp32 q/k/v still the split).  These cases put the larger forms through ragged
-# chunks, both gates, both layouts and a bf16 pool, each next to a switch.
+# dv = 128 batches of up to 128 (request, head) tiles (every case above) run
+# each tile as two workgroups of 16-column slabs; larger ones as one
+# workgroup per tile with 32-column slabs.  These cases put the larger form
+# through ragged chunks, both gates, both layouts, a bf16 pool and fp32
+# q/k/v, from one tile past the switch to several rounds of the CUs.
 WIDE_GRID = {
     "grid129_vfirst": work("grid129_vfirst", B=3, H_=43, HV=43, DK=128, DV=128, tokens="u:1..60", seed=12,
                            state_layout="v_first"),
@@ -108,10 +108,8 @@ WIDE_GRID = {
     "grid288_kfirst_softplus_bf16_state": work("grid288_kfirst_softplus_bf16_state", B=9, H_=16, HV=32,
                                                DK=128, DV=128, tokens="u:1..40", gate=wl.SOFTPLUS, seed=18,
                                                state_dtype="bf16"),
-    # 512 + 64 tiles: a plain launch for the first 512, a split one for the rest
-    "grid576_split_tail": work("grid576_split_tail", B=9, H_=64, HV=64, DK=128, DV=128, tokens="u:1..20",
-                               gate=wl.SOFTPLUS, seed=20),
-    # fp32 q/k/v take the split at any tile count
+    "grid576_kfirst_softplus": work("grid576_kfirst_softplus", B=9, H_=64, HV=64, DK=128, DV=128,
+                                    tokens="u:1..20", gate=wl.SOFTPLUS, seed=20),
     "grid260_f32_qkv": work("grid260_f32_qkv", B=4, H_=65, HV=65, DK=128, DV=128, tokens="u:1..30", seed=19,
                             qkv="f32", state_layout="v_first"),
 }
