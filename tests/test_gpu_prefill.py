@@ -187,11 +187,19 @@ def test_prefill_varlen_gqa_batch(torch_cuda):
     print("varlen gqa", stats, flush=True)
 
 
-def test_prefill_deterministic_bitwise(torch_cuda):
+@pytest.mark.parametrize("tiles", [16, 160])
+def test_prefill_deterministic_bitwise(torch_cuda, tiles):
+    """Two calls on the same inputs give bit-identical outputs and states, in
+    both launch forms (two workgroups per tile up to 128 tiles, one beyond),
+    whose elementwise and products waves hand tables over through LDS."""
     torch = torch_cuda
-    cfg = work("det", B=4, H_=2, HV=4, DK=128, DV=128, tokens="u:20..70", seed=13,
-               state_layout="v_first")
-    _say("prefill determinism", cfg)
+    if tiles == 16:
+        cfg = work("det", B=4, H_=2, HV=4, DK=128, DV=128, tokens="u:20..70", seed=13,
+                   state_layout="v_first")
+    else:
+        cfg = work("det160", B=5, H_=16, HV=32, DK=128, DV=128, tokens="u:20..70", seed=21,
+                   gate=wl.SOFTPLUS)
+    _say("prefill determinism", tiles, cfg)
     inp = wl.draw(cfg)
     dev = wl.to_device(inp)
     p1 = wl.device_pool(inp)
