@@ -1031,18 +1031,18 @@ kda_prefill_chunks(DecodeArgs a) {
       float sq = 0.0f, sk = 0.0f;
       f32x4 Pp = {0.0f, 0.0f, 0.0f, 0.0f};   // P_raw partial (acc: rows t, column s)
       f32x4 Rp = {0.0f, 0.0f, 0.0f, 0.0f};   // R_raw^T partial (acc: rows s, column t)
-  #pragma unroll
+#pragma unroll
       for (int p = 0; p < NP; ++p) {
         if (w + NW * p >= NG) continue;
         float q[CPL], k[CPL], x[CPL];
-  #pragma unroll
+#pragma unroll
         for (int j = 0; j < CPL; ++j) {     // padding tokens: q = k = 0
           q[j] = live ? qin[p][j] : 0.0f;
           k[j] = live ? kin[p][j] : 0.0f;
           x[j] = xin[p][j];
         }
         float G[CPL], GL[CPL];
-  #pragma unroll
+#pragma unroll
         for (int j = 0; j < CPL; ++j) {
           sq = fmaf(q[j], q[j], sq);
           sk = fmaf(k[j], k[j], sk);
@@ -1050,10 +1050,10 @@ kda_prefill_chunks(DecodeArgs a) {
         // G, GL: Gamma and Gamma_last of the lane's channels, times log2(e)
         log2_decays<CPL>(a.gate_mode, amp, amp2, lb2, live, x, dtb[p], G);
         float gr[CPL];   // the per-token log2-decays themselves, for wide spans
-  #pragma unroll
+#pragma unroll
         for (int j = 0; j < CPL; ++j) gr[j] = G[j];
         bool wide_lane = false;
-  #pragma unroll
+#pragma unroll
         for (int j = 0; j < CPL; ++j) {
           G[j] = row_scan(G[j]);
           GL[j] = dpp_row<kDppRowBcast15, true>(G[j]);
@@ -1070,12 +1070,12 @@ kda_prefill_chunks(DecodeArgs a) {
         bool exact = false;
         if (wide) {
           bool exact_lane = false;
-  #pragma unroll
+#pragma unroll
           for (int j = 0; j < CPL; ++j) exact_lane |= !(-GL[j] <= kExactSpan);
           exact = __any(exact_lane);
         }
         if (!exact) {
-  #pragma unroll
+#pragma unroll
           for (int j = 0; j < CPL; ++j) {
             const float eg = exp2_f(G[j]);
             egl[j] = dpp_row<kDppRowBcast15, true>(eg);   // exp(Gamma_last), from token 15
@@ -1099,15 +1099,15 @@ kda_prefill_chunks(DecodeArgs a) {
             float xg[CPL], gg[CPL];
             xr.unpack(xg);
             log2_decays<CPL>(a.gate_mode, amp, amp2, lb2, live, xg, dtb[p], gg);
-  #pragma unroll
+#pragma unroll
             for (int j = 0; j < CPL; j += 4)
               *reinterpret_cast<f32x4*>(&sh.ex.pg[w][n][CPL * g + j]) = f32x4{gg[j], gg[j + 1], gg[j + 2], gg[j + 3]};
           }
-  #pragma unroll
+#pragma unroll
           for (int j = 0; j < CPL; j += 4) {
             const f32x4 x4 = *reinterpret_cast<const f32x4*>(&sh.ex.pg[w][n][CPL * g + j]);
             f32x4 b4, r4;
-  #pragma unroll
+#pragma unroll
             for (int i = 0; i < 4; ++i) {
               const float gj = fmaxf(x4[i], -kGateFloor);
               const float gb = kGateStep * ceilf(gj * (1.0f / kGateStep));
@@ -1118,11 +1118,11 @@ kda_prefill_chunks(DecodeArgs a) {
             *reinterpret_cast<f32x4*>(&sh.ex.ps[w][n][CPL * g + j]) = r4;
           }
           wave_lds_order();
-  #pragma unroll
+#pragma unroll
           for (int j = 0; j < CPL; j += 4) {
             const f32x4 b4 = *reinterpret_cast<const f32x4*>(&sh.ex.pg[w][n][CPL * g + j]);
             const f32x4 r4 = *reinterpret_cast<const f32x4*>(&sh.ex.ps[w][n][CPL * g + j]);
-  #pragma unroll
+#pragma unroll
             for (int i = 0; i < 4; ++i) {
               const float dlast = (dpp_row<kDppRowBcast15, true>(b4[i]) - b4[i]) +
                                   (dpp_row<kDppRowBcast15, true>(r4[i]) - r4[i]);
@@ -1137,14 +1137,14 @@ kda_prefill_chunks(DecodeArgs a) {
         tab.kt.template store<CPL>(n, chan0[p], kt);
         tab.qt.template store<CPL>(n, chan0[p], qt);
         if (n == 0) {
-  #pragma unroll
+#pragma unroll
           for (int j = 0; j < CPL; j += 4)
             *reinterpret_cast<f32x4*>(&tab.egl[chan0[p] + j]) = f32x4{egl[j], egl[j + 1], egl[j + 2], egl[j + 3]};
         }
         if (!wide) {
           // this group's P and R parts as one product each
           float kp[CPL], qp[CPL], ks[CPL];
-  #pragma unroll
+#pragma unroll
           for (int j = 0; j < CPL; ++j) {
             const float ep = exp2_f(fmaf(-0.5f, GL[j], G[j]));
             kp[j] = k[j] * ep;
@@ -1163,7 +1163,7 @@ kda_prefill_chunks(DecodeArgs a) {
           // over all lanes and channels is the widest block's span.
           float f2[CPL], f4[CPL], f8[CPL];
           float m8 = 0.0f, m4 = 0.0f, m2 = 0.0f;
-  #pragma unroll
+#pragma unroll
           for (int j = 0; j < CPL; ++j) {
             seg_prefix(gr[j], n, f2[j], f4[j], f8[j]);
             m8 = fminf(m8, f8[j]);
@@ -1180,7 +1180,7 @@ kda_prefill_chunks(DecodeArgs a) {
             // prefix sums (no larger than the tier-0 exponents)
             wide_diagonal<8, PREC>(Pw, Rw, f8, k, q, n, g);
             float rx[CPL];
-  #pragma unroll
+#pragma unroll
             for (int j = 0; j < CPL; ++j) rx[j] = dpp_row<kDppRowBcast0 + 7, true>(f8[j]) - f8[j];
             wide_level<8, PREC>(Pw, Rw, f8, rx, k, q, n, g);
           } else {
@@ -1188,16 +1188,16 @@ kda_prefill_chunks(DecodeArgs a) {
             else if (tier == 3) wide_diagonal<2, PREC>(Pw, Rw, f2, k, q, n, g);
             else {   // blocks of one token: R's diagonal is q_t . k_t (P's is unused)
               float qk = 0.0f;
-  #pragma unroll
+#pragma unroll
               for (int j = 0; j < CPL; ++j) qk = fmaf(q[j], k[j], qk);
               qk = cross_row_sum(qk);
-  #pragma unroll
+#pragma unroll
               for (int i = 0; i < 4; ++i) Rw[i] = pair_xor(n, g, i) == 0 ? qk : 0.0f;
             }
             // the lower halves' exponents from suffix sums within blocks of
             // 1, 2, 4, 8 in turn (exact for any span)
             float rs[CPL], rx[CPL];
-  #pragma unroll
+#pragma unroll
             for (int j = 0; j < CPL; ++j) {
               rs[j] = seg_suffix_step<2>(gr[j], n);
               rx[j] = 0.0f;
@@ -1207,11 +1207,11 @@ kda_prefill_chunks(DecodeArgs a) {
               suffix_excl<2>(rx, rs, n);
               wide_level<2, PREC>(Pw, Rw, f2, rx, k, q, n, g);
             }
-  #pragma unroll
+#pragma unroll
             for (int j = 0; j < CPL; ++j) rs[j] = seg_suffix_step<4>(rs[j], n);
             suffix_excl<4>(rx, rs, n);
             wide_level<4, PREC>(Pw, Rw, f4, rx, k, q, n, g);
-  #pragma unroll
+#pragma unroll
             for (int j = 0; j < CPL; ++j) rs[j] = seg_suffix_step<8>(rs[j], n);
             suffix_excl<8>(rx, rs, n);
             wide_level<8, PREC>(Pw, Rw, f8, rx, k, q, n, g);
@@ -1246,7 +1246,7 @@ kda_prefill_chunks(DecodeArgs a) {
       float rk[4], br[4];
       {
         const f32x4 bt = *reinterpret_cast<const f32x4*>(&tab.beta[4 * g]);
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < 4; ++i) {
           rk[i] = rsqrt_f(wave_sum<NW>(&tab.nk[4 * g + i][0]) + a.l2_eps);
           br[i] = bt[i] * rk[i];
@@ -1257,10 +1257,10 @@ kda_prefill_chunks(DecodeArgs a) {
       // -L[t][s] for rows t = 4g + i, column s = n, into the wave's copy
       {
         f32x4 Pf = *reinterpret_cast<const f32x4*>(&tab.pp[0][n][4 * g]);
-  #pragma unroll
+#pragma unroll
         for (int ww = 1; ww < NW; ++ww) Pf += *reinterpret_cast<const f32x4*>(&tab.pp[ww][n][4 * g]);
         const float cs = rkn * tab.beta[n];
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < 4; ++i) sh.neg.nl[w][4 * g + i][n] = n < 4 * g + i ? -(rk[i] * cs * Pf[i]) : 0.0f;
       }
       wave_lds_order();
@@ -1273,13 +1273,13 @@ kda_prefill_chunks(DecodeArgs a) {
       float tc[4];
       {
         float nlt[kChunk];
-  #pragma unroll
+#pragma unroll
         for (int q4 = 0; q4 < kChunk / 4; ++q4) {
           const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sh.neg.nl[w][n][4 * q4]);
-  #pragma unroll
+#pragma unroll
           for (int j = 0; j < 4; ++j) nlt[4 * q4 + j] = l4[j];
         }
-  #pragma unroll
+#pragma unroll
         for (int j = 0; j < 4; ++j) tc[j] = n == 4 * g + j ? 1.0f : 0.0f;
         solve_rows<0, 4>(tc, nlt);
       }
@@ -1287,17 +1287,17 @@ kda_prefill_chunks(DecodeArgs a) {
       float rv[4];
       {
         f32x4 Rf = *reinterpret_cast<const f32x4*>(&tab.rr[0][n][4 * g]);
-  #pragma unroll
+#pragma unroll
         for (int ww = 1; ww < NW; ++ww) Rf += *reinterpret_cast<const f32x4*>(&tab.rr[ww][n][4 * g]);
-  #pragma unroll
+#pragma unroll
         for (int j = 0; j < 4; ++j) rv[j] = 4 * g + j <= n ? Rf[j] : 0.0f;
       }
 
       // X = V - diag(rk) Kt_raw S,  Y^T = S^T Qt_raw^T   (per value tile nt)
       f32x4 X[NTV], YT[NTV];
-  #pragma unroll
+#pragma unroll
       for (int nt = 0; nt < NTV; ++nt) X[nt] = YT[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  #pragma unroll
+#pragma unroll
       for (int s = 0; s < KS; ++s) {
         const Frag<PREC, 8> fk = tab.kt.frag8(n, s, g);
         const Frag<PREC, 8> fq = tab.qt.frag8(n, s, g);
@@ -1305,7 +1305,7 @@ kda_prefill_chunks(DecodeArgs a) {
         // is applied here, on the way to the operands
         const f32x4 e0 = *reinterpret_cast<const f32x4*>(&tab.egl[32 * s + 4 * g]);
         const f32x4 e1 = *reinterpret_cast<const f32x4*>(&tab.egl[32 * s + 16 + 4 * g]);
-  #pragma unroll
+#pragma unroll
         for (int nt = 0; nt < NTV; ++nt) {
           const Frag<PREC, 8> fs = acc_frag8_decay<PREC>(S[2 * s][nt], S[2 * s + 1][nt], e0, e1);
           mma(X[nt], fk, fs);
@@ -1315,11 +1315,11 @@ kda_prefill_chunks(DecodeArgs a) {
       {
         float vv[VPL];
         v_cur.unpack(vv);
-  #pragma unroll
+#pragma unroll
         for (int j = 0; j < VPL; ++j) vv[j] = live ? vv[j] : 0.0f;
-  #pragma unroll
+#pragma unroll
         for (int nt = 0; nt < NTV; ++nt) {
-  #pragma unroll
+#pragma unroll
           for (int i = 0; i < 4; ++i) X[nt][i] *= -rk[i];
           mma_identity<PREC, QBF16, VPL>(X[nt], vv, nt, n, g);
         }
@@ -1332,25 +1332,25 @@ kda_prefill_chunks(DecodeArgs a) {
       const Frag<PREC, 4> ft = make_frag<PREC, 4>(tc);
       const Frag<PREC, 4> fr = make_frag<PREC, 4>(rv);
       Frag<PREC, 4> fu[NTV];
-  #pragma unroll
+#pragma unroll
       for (int nt = 0; nt < NTV; ++nt) {
         f32x4 U = {0.0f, 0.0f, 0.0f, 0.0f};
         mma<PREC, 4, true>(U, ft, acc_frag4<PREC>(X[nt]));
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < 4; ++i) U[i] *= br[i];
         fu[nt] = acc_frag4<PREC>(U);
         f32x4 OT = YT[nt];
         mma(OT, fu[nt], fr);
         if (live) {
-  #pragma unroll
+#pragma unroll
           for (int i = 0; i < 4; ++i) OT[i] *= rqn;
           store4<QBF16>(a.out, (static_cast<int64_t>(c0 + n) * a.HV + hv) * DV + vcol0 + 16 * nt + 4 * g, OT);
         }
       }
-  #pragma unroll
+#pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const Frag<PREC, 4> fk = tab.kup.frag4(16 * mt + n, g);
-  #pragma unroll
+#pragma unroll
         for (int nt = 0; nt < NTV; ++nt) mma(S[mt][nt], fk, fu[nt]);
       }
     }
