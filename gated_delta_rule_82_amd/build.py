@@ -83,21 +83,27 @@ def build(verbose: bool = True) -> str:
     os.makedirs(LIBDIR, exist_ok=True)
     hipcc = _hipcc()
     api_o = os.path.join(BUILD, "kda_api.o")
-    kernels = ("kda_decode", "kda_prefill", "bench_copy")
-    objs = [os.path.join(BUILD, f"{name}.o") for name in kernels]
+    # (source, object, extra defines): the prefill file once per dk, each
+    # object holding that dk's kernels
+    units = [("kda_decode", "kda_decode", [])]
+    units += [("kda_prefill", f"kda_prefill_dk{dk}", [f"-DKDA_PREFILL_DK={dk}"]) for dk in (32, 64, 128)]
+    lib_objs = [os.path.join(BUILD, f"{obj}.o") for _, obj, _ in units]
+    bench_o = os.path.join(BUILD, "bench_copy.o")
+    units.append(("bench_copy", "bench_copy", []))
     _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", f"-I{INCLUDE}", f"-I{CSRC}",
           "-c", os.path.join(CSRC, "kda_api.cpp"), "-o", api_o], verbose)
-    # the kernel files compile in parallel (each takes tens of seconds)
-    cmds = [[hipcc, *HIP_FLAGS, *EXTRA_FLAGS.get(name, []), f"-I{INCLUDE}", f"-I{CSRC}", "-c",
-             os.path.join(CSRC, f"{name}.hip"), "-o", obj] for name, obj in zip(kernels, objs)]
+    # the kernel objects compile in parallel (each takes tens of seconds)
+    cmds = [[hipcc, *HIP_FLAGS, *EXTRA_FLAGS.get(src, []), *defs, f"-I{INCLUDE}", f"-I{CSRC}", "-c",
+             os.path.join(CSRC, f"{src}.hip"), "-o", os.path.join(BUILD, f"{obj}.o")]
+            for src, obj, defs in units]
     _run_all(cmds, verbose)
     tmp = LIB + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", api_o, *objs[:2], "-o", tmp,
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", api_o, *lib_objs, "-o", tmp,
           "-Wl,-z,defs", "-Wl,--no-undefined",
           f"-Wl,--version-script={os.path.join(CSRC, 'libkda.map')}"], verbose)
     os.replace(tmp, LIB)
     tmp = BENCH_LIB + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", objs[2], "-o", tmp,
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", bench_o, "-o", tmp,
           "-Wl,-z,defs", "-Wl,--no-undefined"], verbose)
     os.replace(tmp, BENCH_LIB)
     return LIB

@@ -61,6 +61,20 @@ bool aligned(const kda_tensor* t, uintptr_t bytes) {
 
 }  // namespace
 
+namespace kda {
+
+int launch_prefill(const DecodeArgs& args, int dk, int dv, bool qkv_bf16, bool state_bf16,
+                   int state_layout, int matmul, hipStream_t stream) {
+  switch (dk) {
+    case 32: return launch_prefill_dk<32>(args, dv, qkv_bf16, state_bf16, state_layout, matmul, stream);
+    case 64: return launch_prefill_dk<64>(args, dv, qkv_bf16, state_bf16, state_layout, matmul, stream);
+    case 128: return launch_prefill_dk<128>(args, dv, qkv_bf16, state_bf16, state_layout, matmul, stream);
+    default: return KDA_ERR_UNSUPPORTED;
+  }
+}
+
+}  // namespace kda
+
 extern "C" {
 
 int kda_abi_version(void) { return KDA_ABI_VERSION; }

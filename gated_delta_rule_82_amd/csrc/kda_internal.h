@@ -52,9 +52,23 @@ int launch_decode(const DecodeArgs& args, int dk, int dv, bool qkv_bf16, bool st
                   int state_layout, bool conv_v, hipStream_t stream);
 
 // Enqueue the chunked prefill kernel (dk, dv in {32, 64, 128}; matmul an
-// enum kda_matmul).  Same return codes.  Defined in kda_prefill.hip.
+// enum kda_matmul).  Same return codes.  Defined in kda_api.cpp.
 int launch_prefill(const DecodeArgs& args, int dk, int dv, bool qkv_bf16, bool state_bf16,
                    int state_layout, int matmul, hipStream_t stream);
+
+// The same for one dk: kda_prefill.hip is compiled once per dk
+// (KDA_PREFILL_DK = 32, 64, 128), each object defining its dk's
+// specialization, so that the three compile in parallel; launch_prefill
+// (kda_api.cpp) picks one.
+template <int DK>
+int launch_prefill_dk(const DecodeArgs& args, int dv, bool qkv_bf16, bool state_bf16, int state_layout,
+                      int matmul, hipStream_t stream);
+template <>
+int launch_prefill_dk<32>(const DecodeArgs&, int, bool, bool, int, int, hipStream_t);
+template <>
+int launch_prefill_dk<64>(const DecodeArgs&, int, bool, bool, int, int, hipStream_t);
+template <>
+int launch_prefill_dk<128>(const DecodeArgs&, int, bool, bool, int, int, hipStream_t);
 
 // Enqueue the q/k convolution kernel.  Same return codes.
 int launch_conv_qk(const ConvQKArgs& args, int dk, bool x_bf16, hipStream_t stream);

@@ -1399,19 +1399,28 @@ int launch_one(const DecodeArgs& a, hipStream_t stream) {
 // workgroups (eight 2048-token requests over 96 heads: 1132 -> 1087 us,
 // softplus 1328 -> 1291 us; 384 tiles 719 -> 679 us; 1536 tiles, three
 // full rounds of the plain form, 1096 -> 1105 us), and it spills less with
-// fp32 q/k/v.  Up to 128 tiles each tile is two workgroups of 16-column
-// slabs, so that twice as many CUs work (one 16 384-token prompt over 96
-// heads: 2.32 ms, against 3.80 ms as one plain workgroup per tile).
-constexpr int64_t kNarrowMaxTiles = 128;   // half of MI355X's 256 CUs
+// fp32 q/k/v.  dv = 64 takes it while one round of it (two four-wave
+// workgroups per CU) holds the batch: the plain two-wave workgroups fit four
+// per CU and, at dk = dv = 64, hold 1024 tiles in one round (2048-token
+// requests over 96 heads: 192 tiles 370 -> 204 us, 512 tiles 546 -> 321 us,
+// 576 546 -> 549 us, 768 550 -> 565 us).  Up to 128 tiles each tile is two
+// workgroups of 16-column slabs, so that twice as many CUs work (one 16
+// 384-token prompt over 96 heads: 2.32 ms against 3.80 ms as one plain
+// workgroup per tile at dv = 128; 1.49 ms against 2.91 ms at dv = 64).
+constexpr int64_t kCUs = 256;   // MI355X
+constexpr int64_t kNarrowMaxTiles = kCUs / 2;
+constexpr int64_t kSplitMaxTiles64 = 2 * kCUs;
 
 template <int DK, int DV, bool QBF16, bool SBF16, bool VFIRST, int PREC>
 int pick_slab(const DecodeArgs& a, hipStream_t s) {
-  if constexpr (DV != 128) {
+  const int64_t tiles = static_cast<int64_t>(a.B) * a.HV;
+  if constexpr (DV == 32) {
     return launch_one<DK, DV, QBF16, SBF16, VFIRST, PREC, kSlabCols, false>(a, s);
   } else {
-    return static_cast<int64_t>(a.B) * a.HV <= kNarrowMaxTiles
-               ? launch_one<DK, DV, QBF16, SBF16, VFIRST, PREC, kNarrowSlabCols, true>(a, s)
-               : launch_one<DK, DV, QBF16, SBF16, VFIRST, PREC, kSlabCols, true>(a, s);
+    if (tiles <= kNarrowMaxTiles) return launch_one<DK, DV, QBF16, SBF16, VFIRST, PREC, kNarrowSlabCols, true>(a, s);
+    if constexpr (DV == 64)
+      if (tiles > kSplitMaxTiles64) return launch_one<DK, DV, QBF16, SBF16, VFIRST, PREC, kSlabCols, false>(a, s);
+    return launch_one<DK, DV, QBF16, SBF16, VFIRST, PREC, kSlabCols, true>(a, s);
   }
 }
 
@@ -1443,15 +1452,14 @@ int pick_dv(const DecodeArgs& a, int dv, bool qbf16, bool sbf16, bool vfirst, in
 
 }  // namespace
 
-int launch_prefill(const DecodeArgs& args, int dk, int dv, bool qkv_bf16, bool state_bf16,
-                   int state_layout, int matmul, hipStream_t stream) {
-  const bool vfirst = state_layout == KDA_STATE_V_FIRST;
-  switch (dk) {
-    case 32: return pick_dv<32>(args, dv, qkv_bf16, state_bf16, vfirst, matmul, stream);
-    case 64: return pick_dv<64>(args, dv, qkv_bf16, state_bf16, vfirst, matmul, stream);
-    case 128: return pick_dv<128>(args, dv, qkv_bf16, state_bf16, vfirst, matmul, stream);
-    default: return KDA_ERR_UNSUPPORTED;
-  }
+// This object's dk (the build compiles this file once per dk).
+#ifdef KDA_PREFILL_DK
+template <>
+int launch_prefill_dk<KDA_PREFILL_DK>(const DecodeArgs& args, int dv, bool qkv_bf16, bool state_bf16,
+                                      int state_layout, int matmul, hipStream_t stream) {
+  return pick_dv<KDA_PREFILL_DK>(args, dv, qkv_bf16, state_bf16, state_layout == KDA_STATE_V_FIRST, matmul,
+                                 stream);
 }
+#endif
 
 }  // namespace kda

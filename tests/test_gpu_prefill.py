@@ -115,6 +115,18 @@ WIDE_GRID = {
 }
 
 
+# dv = 64: up to 128 tiles two workgroups per tile, up to 512 one stage-split
+# workgroup per tile, beyond that the plain two-wave workgroups.
+WIDE_GRID.update({
+    "dv64_grid200_softplus": work("dv64_grid200_softplus", B=5, H_=20, HV=40, DK=64, DV=64, tokens="u:1..60",
+                                  gate=wl.SOFTPLUS, seed=22),
+    "dv64_grid512_dk128_bf16_state": work("dv64_grid512_dk128_bf16_state", B=8, H_=64, HV=64, DK=128, DV=64,
+                                          tokens="u:1..30", seed=23, state_dtype="bf16", state_layout="v_first"),
+    "dv64_grid513_f32_qkv": work("dv64_grid513_f32_qkv", B=9, H_=57, HV=57, DK=64, DV=64, tokens="u:1..25",
+                                 seed=24, qkv="f32"),
+})
+
+
 @pytest.mark.parametrize("matmul", MATMULS)
 @pytest.mark.parametrize("name", sorted(WIDE_GRID))
 def test_prefill_wide_grid(torch_cuda, name, matmul):
