@@ -27,8 +27,10 @@
 //   X = V - diag(rk) (Kt_raw S0),  O = diag(rq) (Qt_raw S0 + R_raw U'),
 //   S = diag(exp(Gamma_last)) S0 + Kup_raw^T U',  U' = diag(beta rk) U,
 //   L = diag(rk) P_raw diag(rk beta).
-// A ragged last chunk is padded with tokens whose q, k, v, beta and g are
-// zero; they change nothing.
+// A ragged last chunk is padded with tokens whose v, beta and g are zero (q
+// and k repeat the last real token's row): with beta = 0 a padding token
+// writes nothing to the state, and as L and R are lower triangular no real
+// token's row reads one, so they change nothing.
 //
 // P_raw and R_raw are sums over the key channels, so each wave adds up the
 // part of its own channels.  For a channel set whose decay span
@@ -244,12 +246,25 @@ __device__ __forceinline__ void mma(f32x4& acc, const Frag<PREC, N>& a, const Fr
 
 // acc += A I_nt where I_nt is the identity restricted to value tile nt: the
 // K = 4N indices (g, j) stand for the slab's columns N g + j, B[(g, j)][n] =
-// [N g + j == 16 nt + n].  A bf16 value is exact in the hi part alone.
+// [N g + j == 16 nt + n].  A bf16 value is exact in the hi part alone, so
+// bf16 A enters the matrix instruction as loaded.
+template <bool BF16, int N>
+struct RunN;
 template <int PREC, bool EXACT_BF16, int N>
-__device__ __forceinline__ void mma_identity(f32x4& acc, const float (&a)[N], int nt, int n, int g) {
+__device__ __forceinline__ void mma_identity(f32x4& acc, const RunN<EXACT_BF16, N>& run, int nt, int n, int g) {
   float e[N];
 #pragma unroll
   for (int j = 0; j < N; ++j) e[j] = N * g + j == 16 * nt + n ? 1.0f : 0.0f;
+  if constexpr (PREC == KDA_MATMUL_SPLIT_BF16 && EXACT_BF16) {
+    typedef typename Frag<PREC, N>::vec vec;
+    const vec va = __builtin_bit_cast(vec, run.w);
+    const Frag<PREC, N> fe = make_frag<PREC, N>(e);
+    if constexpr (N == 8) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, fe.hi, acc, 0, 0, 0);
+    else acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(widen(va), widen(fe.hi), acc, 0, 0, 0);
+    return;
+  }
+  float a[N];
+  run.unpack(a);
   if constexpr (PREC == KDA_MATMUL_F32) {
 #pragma unroll
     for (int j = 0; j < N; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], e[j], acc, 0, 0, 0);
@@ -352,8 +367,8 @@ struct RowTable<KDA_MATMUL_SPLIT_BF16, DK, KERNEL> {
   }
 };
 
-// Kup_raw^T [channel][token] in LDS, written one value at a time by the
-// lane that owns (token, channel) and read as K = 16 fragments of four
+// Kup_raw^T [channel][token] in LDS, written two channels at a time by the
+// lane that owns the token and read as K = 16 fragments of four
 // consecutive tokens.  The split form keeps, per channel and group of four
 // tokens, the four hi parts and then the four lo parts: one 16-byte read is
 // the fragment as the matrix instruction takes it.
@@ -363,7 +378,10 @@ struct KupTable;
 template <int DK, int KERNEL>
 struct KupTable<KDA_MATMUL_F32, DK, KERNEL> {
   float v[DK][kPT];
-  __device__ __forceinline__ void store(int d, int t, float x) { v[d][t] = x; }
+  __device__ __forceinline__ void store2(int d, int t, float x0, float x1) {
+    v[d][t] = x0;
+    v[d + 1][t] = x1;
+  }
   __device__ __forceinline__ Frag<KDA_MATMUL_F32, 4> frag4(int row, int g) const {
     return acc_frag4<KDA_MATMUL_F32>(*reinterpret_cast<const f32x4*>(&v[row][4 * g]));
   }
@@ -373,10 +391,21 @@ template <int DK, int KERNEL>
 struct KupTable<KDA_MATMUL_SPLIT_BF16, DK, KERNEL> {
   static constexpr int P = kChunk / 4 * 8 + 8;   // bf16 per channel row, padded
   __bf16 v[DK][P];
-  __device__ __forceinline__ void store(int d, int t, float x) {
-    const bf16x2 h = {static_cast<__bf16>(x), static_cast<__bf16>(x)};
-    v[d][8 * (t / 4) + t % 4] = h[1];
-    v[d][8 * (t / 4) + 4 + t % 4] = static_cast<__bf16>(minus_hi(h, 1, x));
+  // channels d and d + 1 of token t: one conversion for the two hi parts,
+  // one for the two lo parts.  The packed words are passed through an empty
+  // asm so that the compiler stores their upper halves as they are instead
+  // of converting each value again into a lower half.
+  __device__ __forceinline__ void store2(int d, int t, float x0, float x1) {
+    const bf16x2 h = {static_cast<__bf16>(x0), static_cast<__bf16>(x1)};
+    const bf16x2 l = {static_cast<__bf16>(minus_hi(h, 0, x0)), static_cast<__bf16>(minus_hi(h, 1, x1))};
+    uint32_t hw = __builtin_bit_cast(uint32_t, h), lw = __builtin_bit_cast(uint32_t, l);
+    asm("" : "+v"(hw), "+v"(lw));
+    uint16_t* const r0 = reinterpret_cast<uint16_t*>(&v[d][8 * (t / 4) + t % 4]);
+    uint16_t* const r1 = reinterpret_cast<uint16_t*>(&v[d + 1][8 * (t / 4) + t % 4]);
+    r0[0] = static_cast<uint16_t>(hw);
+    r1[0] = static_cast<uint16_t>(hw >> 16);
+    r0[4] = static_cast<uint16_t>(lw);
+    r1[4] = static_cast<uint16_t>(lw >> 16);
   }
   __device__ __forceinline__ Frag<KDA_MATMUL_SPLIT_BF16, 4> frag4(int row, int g) const {
     const bf16x8 w = *reinterpret_cast<const bf16x8*>(&v[row][8 * g]);
@@ -455,8 +484,11 @@ template <bool BF16, int N>
 struct RunN {
   static constexpr int W = BF16 ? N / 2 : N;
   uint32_t w[W];
-  __device__ __forceinline__ void load(const void* base, int64_t off) {
-    const char* b = static_cast<const char*>(base) + off * (BF16 ? 2 : 4);
+  // from a byte offset to a base pointer; with a uniform base and a 32-bit
+  // offset the load takes the base from scalar registers and the offset from
+  // one vector register (no 64-bit address arithmetic per lane)
+  __device__ __forceinline__ void load(const char* base, uint32_t byte_off) {
+    const char* b = base + byte_off;
     if constexpr (W == 2) {
       const u32x2 x = *reinterpret_cast<const u32x2*>(b);
       w[0] = x[0];
@@ -482,15 +514,16 @@ struct RunN {
 
 // 4 consecutive output values of one token (bf16: the conversion
 // instruction, round to nearest even).
+// (a byte offset to a base pointer, as RunN::load)
 template <bool BF16>
-__device__ __forceinline__ void store4(void* base, int64_t off, const f32x4& x) {
+__device__ __forceinline__ void store4(char* base, uint32_t byte_off, const f32x4& x) {
   if constexpr (BF16) {
     bf16x4 p;
 #pragma unroll
     for (int i = 0; i < 4; ++i) p[i] = static_cast<__bf16>(x[i]);
-    *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(base) + off) = p;
+    *reinterpret_cast<bf16x4*>(base + byte_off) = p;
   } else {
-    *reinterpret_cast<f32x4*>(static_cast<float*>(base) + off) = x;
+    *reinterpret_cast<f32x4*>(base + byte_off) = x;
   }
 }
 
@@ -507,6 +540,21 @@ constexpr int kDppRowBcast0 = 0x150;    // row_newbcast:s = 0x150 + s, lane s of
 constexpr int kDppRowBcast15 = 0x15F;
 
 __device__ __forceinline__ float exp2_f(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// inclusive prefix sums over the 16 lanes of each row, of N values at once
+// (step by step across the values, so that consecutive DPP reads do not
+// depend on each other)
+template <int N>
+__device__ __forceinline__ void row_scan_n(float (&x)[N]) {
+#pragma unroll
+  for (int j = 0; j < N; ++j) x[j] += dpp_row<kDppRowShr1, true>(x[j]);
+#pragma unroll
+  for (int j = 0; j < N; ++j) x[j] += dpp_row<kDppRowShr2, true>(x[j]);
+#pragma unroll
+  for (int j = 0; j < N; ++j) x[j] += dpp_row<kDppRowShr4, true>(x[j]);
+#pragma unroll
+  for (int j = 0; j < N; ++j) x[j] += dpp_row<kDppRowShr8, true>(x[j]);
+}
 
 // inclusive prefix sum over the 16 lanes of each row
 __device__ __forceinline__ float row_scan(float x) {
@@ -959,6 +1007,10 @@ kda_prefill_chunks(DecodeArgs a) {
   const float lb2 = a.lower_bound * kLog2e;
   // the gate bias of the lane's channels, in the form log2_decays takes
   const bool lb_gate = a.gate_mode != KDA_GATE_SOFTPLUS;
+  // Under the lower-bound gate a token's log-decay lies in [lower_bound, 0],
+  // so a chunk spans at most -16 lower_bound: within kSafeSpan (with a margin
+  // for rounding) no chunk needs the wide-span tiers, nor the check for them.
+  const bool narrow_gate = lb_gate && -a.lower_bound * kChunk <= 0.99f * kSafeSpan;
   float dtb[NP][CPL];
   int chan0[NP];
 #pragma unroll
@@ -978,21 +1030,30 @@ kda_prefill_chunks(DecodeArgs a) {
   // Without the split a wave loads its channels' q, k, gates and its slab's
   // v together; with it the elementwise waves load the former, the products
   // waves v.
+  // The rows are addressed from the chunk's first row r0 (a uniform base)
+  // plus the lane's row offset dr (a 32-bit byte offset).
+  constexpr int kIn = QBF16 ? 2 : 4;   // bytes per q, k, v element
   auto load_inputs = [&](ChunkInputs<NP, QBF16, CGS, VC>& in, int c0) {
-    const int64_t tok = c0 + n < t1 ? c0 + n : t1 - 1;
+    const int r0 = c0 < t1 ? c0 : t1 - 1;
+    const uint32_t dr = static_cast<uint32_t>(n < t1 - 1 - r0 ? n : t1 - 1 - r0);
     if (e_wave) {
+      const char* const qb = static_cast<const char*>(a.q) + ((static_cast<int64_t>(r0) * a.H + h) * DK) * kIn;
+      const char* const kb = static_cast<const char*>(a.k) + ((static_cast<int64_t>(r0) * a.H + h) * DK) * kIn;
+      const char* const xb = reinterpret_cast<const char*>(a.raw_gate) + ((static_cast<int64_t>(r0) * a.HV + hv) * DK) * 4;
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
         if (NG % NW == 0 || w + NW * p < NG) {
-          const int64_t qk_off = (tok * a.H + h) * DK + chan0[p];
-          in.q[p].load(a.q, qk_off);
-          in.k[p].load(a.k, qk_off);
-          in.x[p].load(a.raw_gate, (tok * a.HV + hv) * DK + chan0[p]);
+          const uint32_t qk_off = (dr * static_cast<uint32_t>(a.H * DK) + chan0[p]) * kIn;
+          in.q[p].load(qb, qk_off);
+          in.k[p].load(kb, qk_off);
+          in.x[p].load(xb, (dr * static_cast<uint32_t>(a.HV * DK) + chan0[p]) * 4);
         }
       }
-      in.bl = a.beta_logits[tok * a.HV + hv];
+      in.bl = a.beta_logits[(static_cast<int64_t>(r0) * a.HV + hv) + dr * static_cast<uint32_t>(a.HV)];
     }
-    if (p_wave) in.v.load(a.v, (tok * a.HV + hv) * DV + vcol0 + VPL * g);
+    if (p_wave)
+      in.v.load(static_cast<const char*>(a.v) + ((static_cast<int64_t>(r0) * a.HV + hv) * DV) * kIn,
+                (dr * static_cast<uint32_t>(a.HV * DV) + vcol0 + VPL * g) * kIn);
   };
 
   // One input buffer: each chunk first takes its inputs out of it (q, k
@@ -1016,15 +1077,25 @@ kda_prefill_chunks(DecodeArgs a) {
       const int c0 = ce;
       const int m = t1 - c0 < kChunk ? t1 - c0 : kChunk;
       const bool live = n < m;
-      float qin[NP][CPL], kin[NP][CPL], xin[NP][CPL];
+      // This chunk's inputs leave the buffer (q and k widened, the gate
+      // pre-activations turned into log2-decays) before it is refilled with
+      // the next chunk's: the raw words are dead by then, so the refill
+      // loads into the same registers instead of into new ones that the
+      // end of the iteration would copy back.
+      float qin[NP][CPL], kin[NP][CPL], gin[NP][CPL];
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
+        float xin[CPL];
         in.q[p].unpack(qin[p]);
         in.k[p].unpack(kin[p]);
-        in.x[p].unpack(xin[p]);
+        in.x[p].unpack(xin);
+        log2_decays<CPL>(a.gate_mode, amp, amp2, lb2, live, xin, dtb[p], gin[p]);
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) asm volatile("" : "+v"(qin[p][j]), "+v"(kin[p][j]), "+v"(gin[p][j]));
       }
       if constexpr (!SPLIT) v_cur = in.v;
       const float bl_cur = in.bl;
+      asm volatile("" : : "v"(bl_cur) : "memory");
       load_inputs(in, c0 + kChunk);   // past the end: reloads the last row, unused
 
       // ================= stage E: this wave's channels, lane = (token n, quarter g)
@@ -1034,122 +1105,69 @@ kda_prefill_chunks(DecodeArgs a) {
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
         if (w + NW * p >= NG) continue;
-        float q[CPL], k[CPL], x[CPL];
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) {     // padding tokens: q = k = 0
-          q[j] = live ? qin[p][j] : 0.0f;
-          k[j] = live ? kin[p][j] : 0.0f;
-          x[j] = xin[p][j];
-        }
-        float G[CPL], GL[CPL];
+        const float (&q)[CPL] = qin[p];
+        const float (&k)[CPL] = kin[p];
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
           sq = fmaf(q[j], q[j], sq);
           sk = fmaf(k[j], k[j], sk);
         }
-        // G, GL: Gamma and Gamma_last of the lane's channels, times log2(e)
-        log2_decays<CPL>(a.gate_mode, amp, amp2, lb2, live, x, dtb[p], G);
-        float gr[CPL];   // the per-token log2-decays themselves, for wide spans
+        // G, GL: Gamma and Gamma_last of the lane's channels, times log2(e);
+        // gr the per-token log2-decays themselves, for wide spans
+        float G[CPL], GL[CPL], gr[CPL];
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) gr[j] = G[j];
-        bool wide_lane = false;
+        for (int j = 0; j < CPL; ++j) G[j] = gr[j] = gin[p][j];
+        row_scan_n<CPL>(G);
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-          G[j] = row_scan(G[j]);
-          GL[j] = dpp_row<kDppRowBcast15, true>(G[j]);
-          wide_lane |= !(-GL[j] <= kSafeSpan * kLog2e);
+        for (int j = 0; j < CPL; ++j) GL[j] = dpp_row<kDppRowBcast15, true>(G[j]);
+        bool wide = false;
+        if (!narrow_gate) {   // uniform
+          bool wide_lane = false;
+#pragma unroll
+          for (int j = 0; j < CPL; ++j) wide_lane |= !(-GL[j] <= kSafeSpan * kLog2e);
+          wide = __any(wide_lane);
         }
-        float kt[CPL], qt[CPL], egl[CPL];
+        // Kt, Qt and exp(Gamma_last) of the lane's channels into the tables
+        auto store_rows = [&](const float (&kt)[CPL], const float (&qt)[CPL], const float (&egl)[CPL]) {
+          tab.kt.template store<CPL>(n, chan0[p], kt);
+          tab.qt.template store<CPL>(n, chan0[p], qt);
+          if (n == 0) {
+#pragma unroll
+            for (int j = 0; j < CPL; j += 4)
+              *reinterpret_cast<f32x4*>(&tab.egl[chan0[p] + j]) = f32x4{egl[j], egl[j + 1], egl[j + 2], egl[j + 3]};
+          }
+        };
         // Kup's factor exp(Gamma_last - Gamma_s) is exactly 1 for the last
         // real token.  In a ragged chunk Gamma_last is read from lane 15,
         // whose prefix sum holds the same terms as lane m - 1's (the padding
         // adds zeros) added in another order, so the difference would be an
         // ulp of |Gamma| instead of 0.
         const bool last_real = n == m - 1;
-        const bool wide = __any(wide_lane);
-        bool exact = false;
-        if (wide) {
-          bool exact_lane = false;
-#pragma unroll
-          for (int j = 0; j < CPL; ++j) exact_lane |= !(-GL[j] <= kExactSpan);
-          exact = __any(exact_lane);
-        }
-        if (!exact) {
-#pragma unroll
-          for (int j = 0; j < CPL; ++j) {
-            const float eg = exp2_f(G[j]);
-            egl[j] = dpp_row<kDppRowBcast15, true>(eg);   // exp(Gamma_last), from token 15
-            kt[j] = k[j] * eg;
-            qt[j] = q[j] * eg;
-            tab.kup.store(chan0[p] + j, n, last_real ? k[j] : k[j] * exp2_f(GL[j] - G[j]));
-          }
-        } else {
-          // Gamma again, as Gb + Gs: Gb the prefix sums of the gates' integer
-          // parts (exact), Gs those of the remainders (at most 16 in
-          // magnitude).  A difference Gamma_t - Gamma_s is then
-          // an exact difference plus a small one, whatever the decays before
-          // s: no cancellation against a large prefix, and no inf - inf.
-          // The per-token gates again, from the raw gate row (same arithmetic,
-          // same values), then two passes through this lane's table rows, four
-          // channels at a time, so few values are live at once.
-          {
-            const int64_t tok = c0 + n < t1 ? c0 + n : t1 - 1;
-            RunN<false, CPL> xr;
-            xr.load(a.raw_gate, (tok * a.HV + hv) * DK + chan0[p]);
-            float xg[CPL], gg[CPL];
-            xr.unpack(xg);
-            log2_decays<CPL>(a.gate_mode, amp, amp2, lb2, live, xg, dtb[p], gg);
-#pragma unroll
-            for (int j = 0; j < CPL; j += 4)
-              *reinterpret_cast<f32x4*>(&sh.ex.pg[w][n][CPL * g + j]) = f32x4{gg[j], gg[j + 1], gg[j + 2], gg[j + 3]};
-          }
-#pragma unroll
-          for (int j = 0; j < CPL; j += 4) {
-            const f32x4 x4 = *reinterpret_cast<const f32x4*>(&sh.ex.pg[w][n][CPL * g + j]);
-            f32x4 b4, r4;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float gj = fmaxf(x4[i], -kGateFloor);
-              const float gb = kGateStep * ceilf(gj * (1.0f / kGateStep));
-              b4[i] = row_scan(gb);
-              r4[i] = row_scan(gj - gb);
-            }
-            *reinterpret_cast<f32x4*>(&sh.ex.pg[w][n][CPL * g + j]) = b4;
-            *reinterpret_cast<f32x4*>(&sh.ex.ps[w][n][CPL * g + j]) = r4;
-          }
-          wave_lds_order();
-#pragma unroll
-          for (int j = 0; j < CPL; j += 4) {
-            const f32x4 b4 = *reinterpret_cast<const f32x4*>(&sh.ex.pg[w][n][CPL * g + j]);
-            const f32x4 r4 = *reinterpret_cast<const f32x4*>(&sh.ex.ps[w][n][CPL * g + j]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float dlast = (dpp_row<kDppRowBcast15, true>(b4[i]) - b4[i]) +
-                                  (dpp_row<kDppRowBcast15, true>(r4[i]) - r4[i]);
-              const float eg = exp2_f(b4[i] + r4[i]);
-              egl[j + i] = dpp_row<kDppRowBcast15, true>(eg);
-              kt[j + i] = k[j + i] * eg;
-              qt[j + i] = q[j + i] * eg;
-              tab.kup.store(chan0[p] + j + i, n, last_real ? k[j + i] : k[j + i] * exp2_f(dlast));
-            }
-          }
-        }
-        tab.kt.template store<CPL>(n, chan0[p], kt);
-        tab.qt.template store<CPL>(n, chan0[p], qt);
-        if (n == 0) {
-#pragma unroll
-          for (int j = 0; j < CPL; j += 4)
-            *reinterpret_cast<f32x4*>(&tab.egl[chan0[p] + j]) = f32x4{egl[j], egl[j + 1], egl[j + 2], egl[j + 3]};
-        }
-        if (!wide) {
-          // this group's P and R parts as one product each
+        if (!wide) {   // uniform
+          // This group's P and R parts as one product each, of Kp = k
+          // exp(Gamma - c) and Ks = k exp(c - Gamma), c = Gamma_last / 2 (Qp
+          // likewise).  Token 15's exp(Gamma - c) is exp(c), so the tables
+          // take the same exponentials: Kt = Kp exp(c), Qt = Qp exp(c), Kup =
+          // Ks exp(c), exp(Gamma_last) = exp(c)^2.
           float kp[CPL], qp[CPL], ks[CPL];
+          {
+            float ec[CPL], kt[CPL], qt[CPL], egl[CPL];
 #pragma unroll
-          for (int j = 0; j < CPL; ++j) {
-            const float ep = exp2_f(fmaf(-0.5f, GL[j], G[j]));
-            kp[j] = k[j] * ep;
-            qp[j] = q[j] * ep;
-            ks[j] = k[j] * __builtin_amdgcn_rcpf(ep);
+            for (int j = 0; j < CPL; ++j) {
+              const float ep = exp2_f(fmaf(-0.5f, GL[j], G[j]));
+              ec[j] = dpp_row<kDppRowBcast15, true>(ep);
+              kp[j] = k[j] * ep;
+              qp[j] = q[j] * ep;
+              ks[j] = k[j] * __builtin_amdgcn_rcpf(ep);
+              kt[j] = kp[j] * ec[j];
+              qt[j] = qp[j] * ec[j];
+              egl[j] = ec[j] * ec[j];
+            }
+            store_rows(kt, qt, egl);
+#pragma unroll
+            for (int j = 0; j < CPL; j += 2)
+              tab.kup.store2(chan0[p] + j, n, last_real ? k[j] : ks[j] * ec[j],
+                             last_real ? k[j + 1] : ks[j + 1] * ec[j + 1]);
           }
           const Frag<PREC, CPL> fkp = make_frag<PREC, CPL>(kp);
           const Frag<PREC, CPL> fks = make_frag<PREC, CPL>(ks);
@@ -1157,6 +1175,69 @@ kda_prefill_chunks(DecodeArgs a) {
           mma(Pp, fkp, fks);    // P[t][s] = Kp[t] . Ks[s]
           mma(Rp, fks, fqp);    // R^T[s][t] = Ks[s] . Qp[t]
         } else {
+          bool exact_lane = false;
+#pragma unroll
+          for (int j = 0; j < CPL; ++j) exact_lane |= !(-GL[j] <= kExactSpan);
+          const bool exact = __any(exact_lane);
+          float kt[CPL], qt[CPL], egl[CPL];
+          if (!exact) {
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) {
+              const float eg = exp2_f(G[j]);
+              egl[j] = dpp_row<kDppRowBcast15, true>(eg);   // exp(Gamma_last), from token 15
+              kt[j] = k[j] * eg;
+              qt[j] = q[j] * eg;
+            }
+#pragma unroll
+            for (int j = 0; j < CPL; j += 2)
+              tab.kup.store2(chan0[p] + j, n, last_real ? k[j] : k[j] * exp2_f(GL[j] - G[j]),
+                             last_real ? k[j + 1] : k[j + 1] * exp2_f(GL[j + 1] - G[j + 1]));
+          } else {
+            // Gamma again, as Gb + Gs: Gb the prefix sums of the gates' integer
+            // parts (exact), Gs those of the remainders (at most 16 in
+            // magnitude).  A difference Gamma_t - Gamma_s is then
+            // an exact difference plus a small one, whatever the decays before
+            // s: no cancellation against a large prefix, and no inf - inf.
+            // The per-token gates go through this lane's table rows, four
+            // channels at a time, so few values are live at once.
+#pragma unroll
+            for (int j = 0; j < CPL; j += 4)
+              *reinterpret_cast<f32x4*>(&sh.ex.pg[w][n][CPL * g + j]) = f32x4{gr[j], gr[j + 1], gr[j + 2], gr[j + 3]};
+#pragma unroll
+            for (int j = 0; j < CPL; j += 4) {
+              const f32x4 x4 = *reinterpret_cast<const f32x4*>(&sh.ex.pg[w][n][CPL * g + j]);
+              f32x4 b4, r4;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const float gj = fmaxf(x4[i], -kGateFloor);
+                const float gb = kGateStep * ceilf(gj * (1.0f / kGateStep));
+                b4[i] = row_scan(gb);
+                r4[i] = row_scan(gj - gb);
+              }
+              *reinterpret_cast<f32x4*>(&sh.ex.pg[w][n][CPL * g + j]) = b4;
+              *reinterpret_cast<f32x4*>(&sh.ex.ps[w][n][CPL * g + j]) = r4;
+            }
+            wave_lds_order();
+#pragma unroll
+            for (int j = 0; j < CPL; j += 4) {
+              const f32x4 b4 = *reinterpret_cast<const f32x4*>(&sh.ex.pg[w][n][CPL * g + j]);
+              const f32x4 r4 = *reinterpret_cast<const f32x4*>(&sh.ex.ps[w][n][CPL * g + j]);
+              float kl[4];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const float dlast = (dpp_row<kDppRowBcast15, true>(b4[i]) - b4[i]) +
+                                    (dpp_row<kDppRowBcast15, true>(r4[i]) - r4[i]);
+                const float eg = exp2_f(b4[i] + r4[i]);
+                egl[j + i] = dpp_row<kDppRowBcast15, true>(eg);
+                kt[j + i] = k[j + i] * eg;
+                qt[j + i] = q[j + i] * eg;
+                kl[i] = last_real ? k[j + i] : k[j + i] * exp2_f(dlast);
+              }
+              tab.kup.store2(chan0[p] + j, n, kl[0], kl[1]);
+              tab.kup.store2(chan0[p] + j + 2, n, kl[2], kl[3]);
+            }
+          }
+          store_rows(kt, qt, egl);
           // hierarchical factoring (see wide_level): the tier from the spans
           // of the aligned blocks of 8, 4 and 2 tokens.  The gates are <= 0,
           // so a block's most negative partial sum is its total: the minimum
@@ -1239,8 +1320,18 @@ kda_prefill_chunks(DecodeArgs a) {
       const int m = t1 - c0 < kChunk ? t1 - c0 : kChunk;
       const bool live = n < m;
       if constexpr (SPLIT) {
-        v_cur = in_v.v;
+        // v of padding tokens zeroed in its storage words, before the
+        // buffer is refilled (as in the elementwise stage)
+#pragma unroll
+        for (int j = 0; j < RunN<QBF16, VPL>::W; ++j) {
+          v_cur.w[j] = live ? in_v.v.w[j] : 0u;
+          asm volatile("" : "+v"(v_cur.w[j]));
+        }
+        asm volatile("" : : : "memory");
         load_inputs(in_v, c0 + kChunk);
+      } else {
+#pragma unroll
+        for (int j = 0; j < RunN<QBF16, VPL>::W; ++j) v_cur.w[j] = live ? v_cur.w[j] : 0u;
       }
       // ================= per wave: norms, L, T, then the slab's products
       float rk[4], br[4];
@@ -1313,15 +1404,11 @@ kda_prefill_chunks(DecodeArgs a) {
         }
       }
       {
-        float vv[VPL];
-        v_cur.unpack(vv);
-#pragma unroll
-        for (int j = 0; j < VPL; ++j) vv[j] = live ? vv[j] : 0.0f;
 #pragma unroll
         for (int nt = 0; nt < NTV; ++nt) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) X[nt][i] *= -rk[i];
-          mma_identity<PREC, QBF16, VPL>(X[nt], vv, nt, n, g);
+          mma_identity<PREC, QBF16, VPL>(X[nt], v_cur, nt, n, g);
         }
       }
 
@@ -1344,7 +1431,8 @@ kda_prefill_chunks(DecodeArgs a) {
         if (live) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) OT[i] *= rqn;
-          store4<QBF16>(a.out, (static_cast<int64_t>(c0 + n) * a.HV + hv) * DV + vcol0 + 16 * nt + 4 * g, OT);
+          store4<QBF16>(static_cast<char*>(a.out) + ((static_cast<int64_t>(c0) * a.HV + hv) * DV) * kIn,
+                        (n * static_cast<uint32_t>(a.HV * DV) + vcol0 + 16 * nt + 4 * g) * kIn, OT);
         }
       }
 #pragma unroll
