@@ -704,7 +704,7 @@ __device__ __forceinline__ void log2_decays(int gate_mode, float amp, float amp2
     for (int j = 0; j < N; ++j) {
       const float z = x[j] + bias[j];
       const float l = __builtin_amdgcn_logf(1.0f + exp2_f(-kLog2e * fabsf(z)));   // log2
-      G[j] = -fmaf(amp2, fmaxf(z, 0.0f), amp * l);
+      G[j] = fmaf(-amp2, fmaxf(z, 0.0f), -amp * l);
     }
   } else {
 #pragma unroll
@@ -933,10 +933,13 @@ kda_prefill_chunks(DecodeArgs a) {
   const int g = lane / 16;               // channel quarter / accumulator row group
 
   // With the split, the stage that bounds a chunk issues first when both of
-  // a SIMD's waves are ready: the products under the lower-bound gate, the
-  // elementwise stage (with its wide-span tiers) under the softplus.
-  if constexpr (SPLIT)
-    if (a.gate_mode == KDA_GATE_SOFTPLUS ? e_wave : p_wave) __builtin_amdgcn_s_setprio(1);
+  // a SIMD's waves are ready: the products, but with 16-column slabs (half a
+  // slab's products against the whole elementwise stage) under the softplus
+  // gate (with its wide-span tiers) the elementwise stage.
+  if constexpr (SPLIT) {
+    const bool elementwise_first = VC == kNarrowSlabCols && a.gate_mode == KDA_GATE_SOFTPLUS;
+    if (elementwise_first ? e_wave : p_wave) __builtin_amdgcn_s_setprio(1);
+  }
 
   // the workgroup's tile, and its part of the tile's value columns
   const uint32_t tile_id = blockIdx.x / NWG;
